@@ -1,0 +1,166 @@
+"""fp64 CPU oracle of column-wise sparse masked attention (test infrastructure).
+
+Only tests, the smoke check and the CPU-baseline leg of the benchmark use this
+module; the library never calls it. It shares no code with the HIP path.
+
+What it computes is the plain definition from the FlashMask README
+("Formulation"): O = softmax(Q K^T / sqrt(d) + M) V, where d is the last
+dimension of Q, and M is the column-wise sparse mask of the README "Overview"
+and the FlashMask-3 abstract: for each key column j, four query-row
+boundaries (LTS, LTE, UTS, UTE). The mask is materialised densely here (the
+O(N^2) form the FlashMask abstract says previous approaches needed), then
+softmax attention and its analytic gradient are evaluated in float64.
+
+Readings of points the pages leave open:
+  * intervals are half-open [start, end) over 0-based query rows;
+  * masked(i, j) = (causal and j > i) or LTS[j] <= i < LTE[j]
+                   or (not causal and UTS[j] <= i < UTE[j]);
+  * a masked score is -inf (zero probability);
+  * a row with every key masked outputs 0, its logsumexp is -inf and it
+    contributes no gradient;
+  * the scale is 1/sqrt(d) with d the Q/K head dim (not the V head dim);
+  * lts None -> no lower interval; lte None -> LTE = N;
+    uts/ute None (non-causal) -> no upper interval.
+
+Vectors are [B, Hm, N] with Hm in {1, H}; head h uses mask row h if Hm == H,
+else row 0.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+
+__all__ = ["dense_mask", "mask_row", "forward", "forward_rows", "backward",
+           "softmax_probs"]
+
+
+def mask_row(vec: Optional[np.ndarray], b: int, h: int) -> Optional[np.ndarray]:
+    """The [N] boundary vector that head h of batch b uses (None stays None)."""
+    if vec is None:
+        return None
+    v = np.asarray(vec)
+    hm = v.shape[1]
+    return v[b, h if hm > 1 else 0].astype(np.int64)
+
+
+def dense_mask(n: int, causal: bool, lts=None, lte=None, uts=None, ute=None,
+               rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Boolean masked[i, j] for rows i (default all) and all columns j.
+
+    Arguments are the [N] vectors of one (batch, head). Follows the interval
+    test stated in the module docstring, term by term.
+    """
+    i = np.arange(n, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    I = i[:, None]
+    J = np.arange(n, dtype=np.int64)[None, :]
+    m = np.zeros((I.shape[0], n), dtype=bool)
+    if causal:
+        m |= J > I
+    if lts is not None:
+        end = np.full(n, n, np.int64) if lte is None else np.asarray(lte, np.int64)
+        m |= (np.asarray(lts, np.int64)[None, :] <= I) & (I < end[None, :])
+    if not causal and uts is not None and ute is not None:
+        m |= (np.asarray(uts, np.int64)[None, :] <= I) & (I < np.asarray(ute, np.int64)[None, :])
+    return m
+
+
+def _scale(d: int, scale: Optional[float]) -> float:
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def softmax_probs(q: np.ndarray, k: np.ndarray, masked: np.ndarray, scale: float):
+    """Row-wise masked softmax of scale * q k^T for one (batch, head).
+
+    q [R, d], k [N, d] in float64, masked [R, N]. Returns (P [R, N], lse [R]);
+    rows with every key masked get P = 0 and lse = -inf.
+    """
+    s = (q @ k.T) * scale
+    s = np.where(masked, -np.inf, s)
+    empty = masked.all(axis=1)
+    m = np.where(empty, 0.0, s.max(axis=1))
+    p = np.exp(s - m[:, None])          # exp(-inf) = 0 on masked entries
+    l = p.sum(axis=1)
+    l_safe = np.where(empty, 1.0, l)
+    P = p / l_safe[:, None]
+    lse = np.where(empty, -np.inf, m + np.log(l_safe))
+    return P, lse
+
+
+def forward_rows(q, k, v, n, causal, lts=None, lte=None, uts=None, ute=None,
+                 rows=None, scale=None, chunk: int = 1024):
+    """Forward of one (batch, head) for the given query rows.
+
+    q [N, d], k [N, d], v [N, dv] (any float dtype, widened exactly to fp64).
+    Returns (O [R, dv], lse [R]). Rows are processed in chunks so that long
+    sequences never hold an N x N matrix.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    sc = _scale(q.shape[-1], scale)
+    rows = np.arange(n) if rows is None else np.asarray(rows, np.int64)
+    o = np.zeros((rows.shape[0], v.shape[-1]))
+    lse = np.zeros(rows.shape[0])
+    for c0 in range(0, rows.shape[0], chunk):
+        r = rows[c0:c0 + chunk]
+        msk = dense_mask(n, causal, lts, lte, uts, ute, rows=r)
+        P, l = softmax_probs(q[r], k, msk, sc)
+        o[c0:c0 + chunk] = P @ v
+        lse[c0:c0 + chunk] = l
+    return o, lse
+
+
+def forward(q, k, v, causal, lts=None, lte=None, uts=None, ute=None,
+            scale=None, heads=None) -> Tuple[np.ndarray, np.ndarray]:
+    """O [B,H,N,dv] and logsumexp [B,H,N] (natural log, scale included).
+
+    ``heads``: optional list of (b, h) pairs to evaluate; other entries stay 0.
+    """
+    B, H, N, _ = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, N, dv))
+    lse = np.zeros((B, H, N))
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in pairs:
+        o[b, h], lse[b, h] = forward_rows(
+            q[b, h], k[b, h], v[b, h], N, causal,
+            mask_row(lts, b, h), mask_row(lte, b, h),
+            mask_row(uts, b, h), mask_row(ute, b, h), scale=scale)
+    return o, lse
+
+
+def backward(q, k, v, do, causal, lts=None, lte=None, uts=None, ute=None,
+             scale=None, heads=None):
+    """Analytic gradients (dQ, dK, dV) of O = softmax(scale Q K^T + M) V given dO.
+
+    With P the masked softmax and dP = dO V^T:
+      dV = P^T dO,  dS = P * (dP - rowsum(P * dP)),  dQ = scale dS K,
+      dK = scale dS^T Q.
+    Rows with every key masked have P = 0 and so contribute nothing.
+    """
+    B, H, N, d = q.shape
+    dv_ = v.shape[-1]
+    dq = np.zeros((B, H, N, d))
+    dk = np.zeros((B, H, N, d))
+    dvv = np.zeros((B, H, N, dv_))
+    sc = _scale(d, scale)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in pairs:
+        Q = np.asarray(q[b, h], np.float64)
+        K = np.asarray(k[b, h], np.float64)
+        V = np.asarray(v[b, h], np.float64)
+        dO = np.asarray(do[b, h], np.float64)
+        msk = dense_mask(N, causal, mask_row(lts, b, h), mask_row(lte, b, h),
+                         mask_row(uts, b, h), mask_row(ute, b, h))
+        P, _ = softmax_probs(Q, K, msk, sc)
+        del msk
+        dvv[b, h] = P.T @ dO
+        dP = dO @ V.T
+        D = (P * dP).sum(axis=1)
+        dS = P * (dP - D[:, None])
+        del dP, P
+        dq[b, h] = sc * (dS @ K)
+        dk[b, h] = sc * (dS.T @ Q)
+    return dq, dk, dvv

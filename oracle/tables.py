@@ -1,0 +1,110 @@
+"""Oracle of the block tables and tile classes (test infrastructure only).
+
+FlashMask uses its column-wise representation to skip work the mask makes
+unnecessary (README "News" and "Overview"; FlashMask abstract). The skipping
+rule used here: reduce each boundary vector to its min and max over a block
+of key columns, then call a (query block, key block) tile
+
+  * fully masked when the causal edge hides it (c0 > r1 - 1), or every column
+    hides every row through the lower interval (max LTS <= r0 and
+    min LTE >= r1), or, non-causal, through the upper interval
+    (max UTS <= r0 and min UTE >= r1);
+  * unmasked when neither causality (causal and c1 - 1 > r0), nor the lower
+    interval (max LTE > r0 and min LTS < r1), nor, non-causal, the upper
+    interval (max UTE > r0 and min UTS < r1) can reach any element;
+  * partial otherwise,
+
+with rows [r0, r1) and columns [c0, c1) clipped to N. Classes: 0 masked
+(skip), 1 partial, 2 unmasked. The rule is conservative: it never calls a
+tile masked or unmasked wrongly, but may call a tile partial that is not.
+
+Missing vectors take their neutral values in the table: no lower interval ->
+LTS = LTE = N; LTE missing -> LTE = N; no upper interval -> UTS = UTE = 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["kblock_minmax", "classify", "classify_counts", "nnz_dense"]
+
+
+def _full(vec, B, hm, n, fill):
+    if vec is None:
+        return np.full((B, hm, n), fill, np.int64)
+    return np.asarray(vec, np.int64)
+
+
+def _neutral(lts, lte, uts, ute, B, hm, n):
+    """The four [B, Hm, N] vectors with neutral values where one is missing."""
+    if lts is None:
+        LTS = np.full((B, hm, n), n, np.int64)
+        LTE = np.full((B, hm, n), n, np.int64)
+    else:
+        LTS = np.asarray(lts, np.int64)
+        LTE = _full(lte, B, hm, n, n)
+    if uts is None or ute is None:
+        UTS = np.zeros((B, hm, n), np.int64)
+        UTE = np.zeros((B, hm, n), np.int64)
+    else:
+        UTS = np.asarray(uts, np.int64)
+        UTE = np.asarray(ute, np.int64)
+    return LTS, LTE, UTS, UTE
+
+
+def kblock_minmax(B, hm, n, block, lts=None, lte=None, uts=None, ute=None):
+    """int32 [B, Hm, ceil(N/block), 8] table.
+
+    Entry order: LTS min, LTS max, LTE min, LTE max, UTS min, UTS max,
+    UTE min, UTE max, each over columns [kb*block, min(N, (kb+1)*block)).
+    Plain loops over key blocks.
+    """
+    vecs = _neutral(lts, lte, uts, ute, B, hm, n)
+    nkb = (n + block - 1) // block
+    out = np.zeros((B, hm, nkb, 8), np.int64)
+    for kb in range(nkb):
+        c0, c1 = kb * block, min(n, (kb + 1) * block)
+        for t, v in enumerate(vecs):
+            seg = v[:, :, c0:c1]
+            out[:, :, kb, 2 * t] = seg.min(axis=2)
+            out[:, :, kb, 2 * t + 1] = seg.max(axis=2)
+    return out.astype(np.int32)
+
+
+def classify(table, n, block_q, block_k, causal):
+    """int8 [B, Hm, ceil(N/block_q), ceil(N/block_k)] tile classes.
+
+    ``table`` must be the kblock_minmax table at granularity block_k.
+    """
+    t = np.asarray(table, np.int64)
+    B, hm, nkb, _ = t.shape
+    nqb = (n + block_q - 1) // block_q
+    out = np.zeros((B, hm, nqb, nkb), np.int8)
+    for b in range(B):
+        for h in range(hm):
+            for qb in range(nqb):
+                r0, r1 = qb * block_q, min(n, (qb + 1) * block_q)
+                for kb in range(nkb):
+                    c0, c1 = kb * block_k, min(n, (kb + 1) * block_k)
+                    lts_mn, lts_mx, lte_mn, lte_mx, uts_mn, uts_mx, ute_mn, ute_mx = t[b, h, kb]
+                    full = (causal and c0 > r1 - 1) \
+                        or (lts_mx <= r0 and lte_mn >= r1) \
+                        or ((not causal) and uts_mx <= r0 and ute_mn >= r1)
+                    if full:
+                        out[b, h, qb, kb] = 0
+                        continue
+                    causal_free = (not causal) or (c1 - 1 <= r0)
+                    lt_free = lte_mx <= r0 or lts_mn >= r1
+                    ut_free = causal or ute_mx <= r0 or uts_mn >= r1
+                    out[b, h, qb, kb] = 2 if (causal_free and lt_free and ut_free) else 1
+    return out
+
+
+def classify_counts(classes) -> np.ndarray:
+    """Histogram [masked, partial, unmasked] of a class map."""
+    c = np.asarray(classes)
+    return np.array([(c == 0).sum(), (c == 1).sum(), (c == 2).sum()], np.int64)
+
+
+def nnz_dense(masked: np.ndarray) -> int:
+    """Count of unmasked (i, j) pairs of a dense boolean mask."""
+    return int(masked.size - np.count_nonzero(masked))

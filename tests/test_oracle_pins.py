@@ -1,0 +1,426 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+* Textbook attention: torch's scaled_dot_product_attention in float64 on the
+  CPU (an independent library routine) for all-open, causal and boolean-mask
+  cases, and its autograd for gradients.
+* Finite differences of L = sum(dO * O) for the analytic backward.
+* Hand-worked fixtures under tests/golden/ (each cites the passage it follows).
+* Closed forms and invariants: block-diagonal documents, shift invariances,
+  rows of P summing to 1, LSE against scipy's logsumexp.
+* Brute force: family definitions versus encoders, tile classes versus a scan
+  of every tile, the nnz closed form versus a dense count.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+import oracle
+from oracle import families
+from sparse_masked_attention_amd import inputs as I
+from sparse_masked_attention_amd import flops
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _sdpa(q, k, v, allowed=None, causal=False, scale=None):
+    """torch SDPA in float64 on the CPU; q,k,v [N, d]."""
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float64))[None, None]
+    mask = None if allowed is None else torch.from_numpy(np.asarray(allowed, bool))[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=mask, is_causal=causal, scale=scale)
+    return o[0, 0].numpy()
+
+
+def _vecs(m: I.Mask):
+    add = lambda x: None if x is None else np.asarray(x)[None, None, :]
+    return dict(lts=add(m.lts), lte=add(m.lte), uts=add(m.uts), ute=add(m.ute))
+
+
+def _rows(m: I.Mask):
+    return dict(lts=m.lts, lte=m.lte, uts=m.uts, ute=m.ute)
+
+
+# ------------------------------------------------------------- P1 families
+
+@pytest.mark.parametrize("seed", range(6))
+def test_encoders_match_definitions(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(40, 300))
+    cases = []
+    lengths = I.random_composition(n, int(rng.integers(1, 6)), rng)
+    cases.append((I.causal_document(n, lengths), families.causal_document(lengths)))
+    q, ans = I.share_question_lengths(n, rng, q_lo=8, q_hi=n // 2, a_lo=2, a_hi=6)
+    cases.append((I.share_question_from(q, ans), families.share_question(q, ans)))
+    w = int(rng.choice([1, 8, 16, 33]))
+    cases.append((I.sliding_window(n, w), families.sliding_window(n, w)))
+    lens, pre = I.prefix_lm_params(n, rng, docs_lo=1, docs_hi=5)
+    cases.append((I.prefix_lm_document_from(lens, pre), families.prefix_lm_document(lens, pre)))
+    blk = int(rng.choice([8, 16]))
+    keep = I.block_sparse_keep(n, rng, blk, 0.5)
+    cases.append((I.block_sparse_from(n, keep, blk), families.block_sparse(n, blk, keep)))
+    cases.append((I.causal_only(n), families.causal(n)))
+    cases.append((I.all_open(n), families.all_open(n)))
+    for m, allowed in cases:
+        masked = oracle.dense_mask(n, m.causal, **_rows(m))
+        assert np.array_equal(~masked, allowed), m.name
+
+
+# ------------------------------------------------------------- golden fixtures
+
+@pytest.mark.parametrize("fname", ["document_n6.json", "prefix_lm_n6.json",
+                                   "out_of_range_empty_row_n4.json"])
+def test_golden_forward(fname):
+    g = json.load(open(os.path.join(GOLDEN, fname)))
+    n = g["n"]
+    vec = {k: (np.array(g[k])[None, None, :] if k in g else None)
+           for k in ("lts", "lte", "uts", "ute")}
+    masked = oracle.dense_mask(n, g["causal"], **{k: (None if v is None else v[0, 0]) for k, v in vec.items()})
+    assert np.array_equal(~masked, np.array(g["allowed"], bool))
+    d = 4
+    q = np.zeros((1, 1, n, d))
+    k = _rand((1, 1, n, d), 3)
+    v = np.array(g["v_column"], float)[None, None, :, None]
+    o, lse = oracle.forward(q, k, v, g["causal"], **vec)
+    np.testing.assert_allclose(o[0, 0, :, 0], g["o_when_q_zero"], atol=1e-15)
+    want = [(-math.inf if s == "-inf" else math.log(int(s[2:]))) for s in g["lse_when_q_zero"]]
+    np.testing.assert_array_equal(np.isinf(lse[0, 0]), np.isinf(want))
+    fin = ~np.isinf(want)
+    np.testing.assert_allclose(lse[0, 0][fin], np.array(want)[fin], atol=1e-15)
+
+
+def test_golden_tile_classes():
+    g = json.load(open(os.path.join(GOLDEN, "sliding_window_classes_n8.json")))
+    lts = np.array(g["lts"])[None, None]
+    lte = np.array(g["lte"])[None, None]
+    tab = oracle.kblock_minmax(1, 1, g["n"], g["block_k"], lts, lte)
+    assert np.array_equal(tab[0, 0], np.array(g["table"]))
+    cls = oracle.classify(tab, g["n"], g["block_q"], g["block_k"], g["causal"])
+    assert np.array_equal(cls[0, 0], np.array(g["classes"]))
+
+
+# ------------------------------------------------------------- P2-P4 forward vs SDPA
+
+@pytest.mark.parametrize("n,d,dv", [(1, 8, 8), (37, 16, 16), (128, 32, 32), (200, 16, 24)])
+def test_forward_all_open_is_plain_attention(n, d, dv):
+    q, k, v = _rand((n, d), 1), _rand((n, d), 2), _rand((n, dv), 3)
+    m = I.all_open(n)
+    o, lse = oracle.forward_rows(q, k, v, n, False, **_rows(m))
+    np.testing.assert_allclose(o, _sdpa(q, k, v), rtol=0, atol=1e-12)
+    s = (q @ k.T) / math.sqrt(d)
+    np.testing.assert_allclose(lse, logsumexp(s, axis=1), atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [1, 5, 64, 150])
+def test_forward_causal_is_sdpa_causal(n):
+    q, k, v = _rand((n, 16), 4), _rand((n, 16), 5), _rand((n, 16), 6)
+    o, _ = oracle.forward_rows(q, k, v, n, True, **_rows(I.causal_only(n)))
+    np.testing.assert_allclose(o, _sdpa(q, k, v, causal=True), atol=1e-12)
+
+
+@pytest.mark.parametrize("family", ["document", "share_question", "sliding_window",
+                                    "prefix_lm_document", "block_sparse", "document3"])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_forward_families_vs_sdpa_bool_mask(family, seed):
+    n, d = 256, 16
+    m = I.make_mask(family, n, np.random.default_rng(seed))
+    q, k, v = _rand((n, d), 10 + seed), _rand((n, d), 20 + seed), _rand((n, d), 30 + seed)
+    allowed = ~oracle.dense_mask(n, m.causal, **_rows(m))
+    assert allowed.any(axis=1).all()          # these families leave every row a key
+    o, lse = oracle.forward_rows(q, k, v, n, m.causal, **_rows(m))
+    np.testing.assert_allclose(o, _sdpa(q, k, v, allowed=allowed), atol=1e-12)
+    s = np.where(allowed, (q @ k.T) / math.sqrt(d), -np.inf)
+    np.testing.assert_allclose(lse, logsumexp(s, axis=1), atol=1e-12)
+
+
+def test_forward_scale_is_head_dim_of_q():
+    n, d, dv = 33, 16, 8
+    q, k, v = _rand((n, d), 1), _rand((n, d), 2), _rand((n, dv), 3)
+    o, _ = oracle.forward_rows(q, k, v, n, False)
+    np.testing.assert_allclose(o, _sdpa(q, k, v, scale=1 / math.sqrt(d)), atol=1e-12)
+    o2, _ = oracle.forward_rows(q, k, v, n, False, scale=0.3)
+    np.testing.assert_allclose(o2, _sdpa(q, k, v, scale=0.3), atol=1e-12)
+
+
+# ------------------------------------------------------------- P5 block-diagonal documents
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_document_is_blockwise_causal(seed):
+    rng = np.random.default_rng(seed)
+    n, d = 120, 8
+    lengths = I.random_composition(n, 4, rng)
+    m = I.causal_document(n, lengths)
+    q, k, v, do = (_rand((1, 1, n, d), 40 + seed + t) for t in range(4))
+    o, _ = oracle.forward(q, k, v, True, **_vecs(m))
+    dq, dk, dv = oracle.backward(q, k, v, do, True, **_vecs(m))
+    s = 0
+    for L in lengths:
+        sl = slice(s, s + L)
+        tq, tk, tv = (torch.from_numpy(x[0, 0, sl].copy()).requires_grad_() for x in (q, k, v))
+        to = torch.nn.functional.scaled_dot_product_attention(tq[None, None], tk[None, None],
+                                                              tv[None, None], is_causal=True)[0, 0]
+        (to * torch.from_numpy(do[0, 0, sl])).sum().backward()
+        np.testing.assert_allclose(o[0, 0, sl], to.detach().numpy(), atol=1e-12)
+        np.testing.assert_allclose(dq[0, 0, sl], tq.grad.numpy(), atol=1e-11)
+        np.testing.assert_allclose(dk[0, 0, sl], tk.grad.numpy(), atol=1e-11)
+        np.testing.assert_allclose(dv[0, 0, sl], tv.grad.numpy(), atol=1e-11)
+        s += L
+
+
+def test_prefix_lm_documents_are_independent():
+    rng = np.random.default_rng(7)
+    n, d = 90, 8
+    lens, pre = I.prefix_lm_params(n, rng, docs_lo=3, docs_hi=3)
+    m = I.prefix_lm_document_from(lens, pre)
+    q, k, v = (_rand((1, 1, n, d), 70 + t) for t in range(3))
+    o, _ = oracle.forward(q, k, v, False, **_vecs(m))
+    s = 0
+    for L, p in zip(lens, pre):
+        sl = slice(s, s + L)
+        allowed = families.prefix_lm_document([L], [p])
+        np.testing.assert_allclose(o[0, 0, sl], _sdpa(q[0, 0, sl], k[0, 0, sl], v[0, 0, sl],
+                                                      allowed=allowed), atol=1e-12)
+        s += L
+
+
+# ------------------------------------------------------------- P6 backward
+
+def _loss(q, k, v, do, causal, vec):
+    o, _ = oracle.forward(q, k, v, causal, **vec)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("family,causal", [("all_open", False), ("causal", True),
+                                           ("document", True), ("prefix", False),
+                                           ("empty_rows", False)])
+def test_backward_finite_differences(family, causal):
+    rng = np.random.default_rng(11)
+    n, d, dv = 14, 4, 3
+    if family == "all_open":
+        m = I.all_open(n)
+    elif family == "causal":
+        m = I.causal_only(n)
+    elif family == "document":
+        m = I.causal_document(n, [5, 4, 5])
+    elif family == "prefix":
+        m = I.prefix_lm_document_from([8, 6], [3, 2])
+    else:   # rows 3 and 4 hidden from every key, plus arbitrary intervals
+        lts = rng.integers(-3, n + 3, n).astype(np.int32)
+        lte = lts + rng.integers(0, 6, n).astype(np.int32)
+        lts[:] = np.minimum(lts, 3)
+        lte[:] = np.maximum(lte, 5)
+        m = I.Mask(n, False, lts, lte, np.zeros(n, np.int32), np.zeros(n, np.int32))
+    vec = _vecs(m)
+    q, k, v, do = _rand((1, 1, n, d), 1), _rand((1, 1, n, d), 2), _rand((1, 1, n, dv), 3), _rand((1, 1, n, dv), 4)
+    dq, dk, dvv = oracle.backward(q, k, v, do, causal, **vec)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dvv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args = dict(q=q, k=k, v=v)
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], do, causal, vec)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], do, causal, vec)
+            num[idx] = (lp - lm) / (2 * h)
+        err = np.abs(num - g).max() / max(1e-12, np.abs(g).max())
+        assert err < 1e-6, (name, err)
+    if family == "empty_rows":
+        masked = oracle.dense_mask(n, causal, **_rows(m))
+        empty = masked.all(axis=1)
+        assert empty[3] and empty[4]
+        assert np.all(dq[0, 0, empty] == 0)
+
+
+@pytest.mark.parametrize("family", ["document", "sliding_window", "share_question", "prefix_lm_document"])
+def test_backward_vs_sdpa_autograd(family):
+    n, d = 96, 16
+    m = I.make_mask(family, n, np.random.default_rng(5))
+    allowed = torch.from_numpy(~oracle.dense_mask(n, m.causal, **_rows(m)))
+    q, k, v, do = (_rand((1, 1, n, d), 80 + t) for t in range(4))
+    dq, dk, dv = oracle.backward(q, k, v, do, m.causal, **_vecs(m))
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=allowed[None, None])
+    (to * torch.from_numpy(do)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-11)
+
+
+# ------------------------------------------------------------- P7, P8 invariants
+
+def test_invariants():
+    rng = np.random.default_rng(3)
+    n, d = 64, 8
+    m = I.make_mask("share_question", n, rng)
+    vec = _vecs(m)
+    q, k, v, do = (_rand((1, 1, n, d), 90 + t) for t in range(4))
+    masked = oracle.dense_mask(n, m.causal, **_rows(m))
+    P, _ = oracle.softmax_probs(q[0, 0], k[0, 0], masked, 1 / math.sqrt(d))
+    np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-14)
+    o, lse = oracle.forward(q, k, v, True, **vec)
+    c = _rand((d,), 99)
+    o_k, _ = oracle.forward(q, k + c, v, True, **vec)
+    np.testing.assert_allclose(o_k, o, atol=1e-12)
+    o_v, _ = oracle.forward(q, k, v + c, True, **vec)
+    np.testing.assert_allclose(o_v, o + c, atol=1e-12)
+    _, _, dv = oracle.backward(q, k, v, do, True, **vec)
+    np.testing.assert_allclose(dv[0, 0].sum(axis=0), do[0, 0].sum(axis=0), atol=1e-12)
+    dq, _, _ = oracle.backward(q, k, v, do, True, **vec)
+    # dS rows sum to zero, so dQ is unchanged when every key gains the same vector c
+    dq_k, _, _ = oracle.backward(q, k + c, v, do, True, **vec)
+    np.testing.assert_allclose(dq_k, dq, atol=1e-11)
+
+
+def test_empty_rows_zero_output_and_gradients():
+    n, d = 16, 8
+    lts = np.zeros(n, np.int32); lte = np.zeros(n, np.int32)
+    lts[:] = 4; lte[:] = 7                      # rows 4..6 hidden from every key
+    m = I.Mask(n, False, lts, lte, np.zeros(n, np.int32), np.zeros(n, np.int32))
+    vec = _vecs(m)
+    q, k, v, do = (_rand((1, 1, n, d), 120 + t) for t in range(4))
+    o, lse = oracle.forward(q, k, v, False, **vec)
+    assert np.all(o[0, 0, 4:7] == 0) and np.all(np.isneginf(lse[0, 0, 4:7]))
+    assert np.all(np.isfinite(lse[0, 0, :4])) and np.all(np.isfinite(lse[0, 0, 7:]))
+    dq, dk, dv = oracle.backward(q, k, v, do, False, **vec)
+    assert np.all(dq[0, 0, 4:7] == 0)
+    do2 = do.copy(); do2[0, 0, 4:7] = 123.0     # dO on empty rows must not matter
+    dq2, dk2, dv2 = oracle.backward(q, k, v, do2, False, **vec)
+    np.testing.assert_array_equal(dk2, dk)
+    np.testing.assert_array_equal(dv2, dv)
+
+
+def test_mask_heads_broadcast_and_per_head():
+    n, d, H = 40, 8, 3
+    rng = np.random.default_rng(0)
+    ms = [I.make_mask("document", n, np.random.default_rng(s)) for s in range(H)]
+    lts = np.stack([m.lts for m in ms])[None]
+    lte = np.stack([m.lte for m in ms])[None]
+    q, k, v = (rng.standard_normal((1, H, n, d)) for _ in range(3))
+    o, _ = oracle.forward(q, k, v, True, lts=lts, lte=lte)
+    for h in range(H):
+        o1, _ = oracle.forward_rows(q[0, h], k[0, h], v[0, h], n, True, ms[h].lts, ms[h].lte)
+        np.testing.assert_allclose(o[0, h], o1, atol=0)
+    o_b, _ = oracle.forward(q, k, v, True, lts=lts[:, :1], lte=lte[:, :1])
+    for h in range(H):
+        o1, _ = oracle.forward_rows(q[0, h], k[0, h], v[0, h], n, True, ms[0].lts, ms[0].lte)
+        np.testing.assert_allclose(o_b[0, h], o1, atol=0)
+
+
+def test_row_subset_matches_full():
+    n, d = 300, 8
+    m = I.make_mask("prefix_lm_document", n, np.random.default_rng(2))
+    q, k, v = (_rand((n, d), 130 + t) for t in range(3))
+    o, lse = oracle.forward_rows(q, k, v, n, False, **_rows(m), chunk=64)
+    rows = np.array([0, 5, 77, 299])
+    o2, lse2 = oracle.forward_rows(q, k, v, n, False, **_rows(m), rows=rows)
+    np.testing.assert_allclose(o2, o[rows], atol=1e-13)
+    np.testing.assert_allclose(lse2, lse[rows], atol=1e-13)
+
+
+# ------------------------------------------------------------- P9 tables and classes
+
+def _brute_classes(masked, n, bq, bk):
+    nqb, nkb = -(-n // bq), -(-n // bk)
+    out = np.zeros((nqb, nkb), np.int8)
+    for a in range(nqb):
+        for b in range(nkb):
+            t = masked[a * bq:(a + 1) * bq, b * bk:(b + 1) * bk]
+            out[a, b] = 0 if t.all() else (2 if not t.any() else 1)
+    return out
+
+
+def _random_vectors(rng, n, spread):
+    lo, hi = -spread, n + spread
+    return (rng.integers(lo, hi, n).astype(np.int32), rng.integers(lo, hi, n).astype(np.int32),
+            rng.integers(lo, hi, n).astype(np.int32), rng.integers(lo, hi, n).astype(np.int32))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_table_is_blockwise_min_max(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 300))
+    bt = int(rng.choice([1, 7, 16, 64]))
+    v4 = _random_vectors(rng, n, 50)
+    tab = oracle.kblock_minmax(1, 1, n, bt, *[x[None, None] for x in v4])
+    cut = np.arange(0, n, bt)
+    for t, x in enumerate(v4):
+        np.testing.assert_array_equal(tab[0, 0, :, 2 * t], np.minimum.reduceat(x, cut))
+        np.testing.assert_array_equal(tab[0, 0, :, 2 * t + 1], np.maximum.reduceat(x, cut))
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("causal", [True, False])
+def test_classes_sound_on_arbitrary_vectors(seed, causal):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 200))
+    bq, bk = int(rng.choice([4, 8, 16, 32])), int(rng.choice([4, 8, 16, 32]))
+    # intervals built from random centres so that some tiles are hidden whole
+    c = rng.integers(-20, n + 20, n)
+    w = rng.integers(0, n + 40, n)
+    lts, lte = (c - w // 2).astype(np.int32), (c + w // 2).astype(np.int32)
+    c2 = rng.integers(-20, n + 20, n)
+    uts, ute = (c2 - w // 3).astype(np.int32), (c2 + w // 3).astype(np.int32)
+    masked = oracle.dense_mask(n, causal, lts, lte, uts, ute)
+    tab = oracle.kblock_minmax(1, 1, n, bk, lts[None, None], lte[None, None], uts[None, None], ute[None, None])
+    cls = oracle.classify(tab, n, bq, bk, causal)[0, 0]
+    brute = _brute_classes(masked, n, bq, bk)
+    assert np.all((cls == 1) | (cls == brute)), "class 0 or 2 must be exact"
+
+
+@pytest.mark.parametrize("family", ["causal", "sliding_window_aligned", "block_sparse"])
+def test_classes_exact_on_block_aligned(family):
+    n, blk = 256, 16
+    rng = np.random.default_rng(1)
+    if family == "causal":
+        m = I.causal_only(n)
+    elif family == "sliding_window_aligned":
+        m = I.sliding_window(n, 64)
+    else:
+        m = I.block_sparse(n, rng, blk, 0.5)
+    masked = oracle.dense_mask(n, True, **_rows(m))
+    tab = oracle.kblock_minmax(1, 1, n, blk, m.lts[None, None], m.lte[None, None])
+    cls = oracle.classify(tab, n, blk, blk, True)[0, 0]
+    np.testing.assert_array_equal(cls, _brute_classes(masked, n, blk, blk))
+
+
+def test_table_neutral_values_for_missing_vectors():
+    n = 10
+    tab = oracle.kblock_minmax(1, 1, n, 4)
+    assert np.all(tab[..., 0:4] == n) and np.all(tab[..., 4:8] == 0)
+    lts = np.arange(n, dtype=np.int32)[None, None]
+    tab = oracle.kblock_minmax(1, 1, n, 4, lts=lts)
+    assert np.all(tab[..., 2:4] == n)
+
+
+# ------------------------------------------------------------- P10 nnz closed form
+
+@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("causal", [True, False])
+def test_nnz_closed_form(seed, causal):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 150))
+    v4 = _random_vectors(rng, n, 30)
+    masked = oracle.dense_mask(n, causal, *v4)
+    got = flops.nnz_columns(n, causal, *v4).sum()
+    assert got == oracle.nnz_dense(masked)
+
+
+def test_nnz_families_and_heads():
+    n = 300
+    for fam in ["document", "share_question", "sliding_window", "prefix_lm_document",
+                "block_sparse", "causal", "all_open"]:
+        m = I.make_mask(fam, n, np.random.default_rng(4))
+        masked = oracle.dense_mask(n, m.causal, **_rows(m))
+        v = _vecs(m)
+        assert flops.nnz(1, 3, n, m.causal, **v) == 3 * oracle.nnz_dense(masked), fam
