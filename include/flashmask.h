@@ -1,0 +1,156 @@
+/*
+ * flashmask.h - C ABI of a gfx950 (MI355X) library for exact attention with a
+ * column-wise sparse mask.
+ *
+ * Operation (FlashMask README, "Formulation"):
+ *     O = softmax(Q K^T / sqrt(d) + M) V
+ * with d the last dimension of Q and M the column-wise sparse mask of the
+ * FlashMask README ("Overview") and the FlashMask-3 abstract: the mask is
+ * indexed by key position and stores, per key column j, query-row interval
+ * bounds. Four int32 vectors of length N describe it:
+ *     row i is masked for column j  <=>  (causal && j > i)
+ *                                     ||  LTS[j] <= i < LTE[j]
+ *                                     ||  (!causal && UTS[j] <= i < UTE[j])
+ * Intervals are half-open over 0-based rows; any int32 value is legal (a value
+ * outside [0, N] acts as if clamped). Masked scores get zero probability. A
+ * row whose keys are all masked outputs 0, has logsumexp -inf and contributes
+ * no gradient. The dense mask never exists: mask memory is O(N) (FlashMask
+ * abstract). Tiles the mask hides completely are skipped, tiles it does not
+ * touch run without mask arithmetic, and only the rest test each element
+ * (FlashMask README "Overview": sparsity is used to skip computation).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers unless stated otherwise. Tensors are
+ *     contiguous row-major: Q, K [B, H, N, d]; V, O, dO [B, H, N, dv];
+ *     logsumexp [B, H, N] float32; mask vectors [B, hm, N] int32 with
+ *     hm == 1 (one mask shared by all heads) or hm == H (one per head).
+ *   - lts == NULL: no lower interval (lte ignored). lte == NULL with lts set:
+ *     LTE = N. Non-causal: uts and ute are both NULL (no upper interval) or
+ *     both set; causal: uts/ute are ignored and may be NULL.
+ *   - The caller owns all memory, including the workspace; the library never
+ *     allocates, frees or synchronises. Every call only enqueues kernels on
+ *     `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *     Results are valid once the caller has synchronised that stream.
+ *   - Arguments are checked on the host before anything is enqueued. A failed
+ *     check returns a status code and touches no output. A failed launch
+ *     returns FM_ERROR_HIP. No exception crosses this interface and the
+ *     library keeps no mutable global state.
+ *   - B * H * N == 0 is a successful no-op. Offsets are 64-bit.
+ *   - softmax_scale <= 0 or NaN selects 1/sqrt(d).
+ *   - Supported: dtype FM_BF16 with d == dv in {64, 128, 256}; FM_FP32 with
+ *     d == dv in {64, 128} (forward and backward). Others: FM_ERROR_NOT_SUPPORTED.
+ */
+#ifndef FLASHMASK_H
+#define FLASHMASK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FM_SUCCESS = 0,
+    FM_ERROR_INVALID_VALUE = 1,       /* NULL required pointer, bad size, hm not in {1, H}, ... */
+    FM_ERROR_NOT_SUPPORTED = 2,       /* (d, dv, dtype) combination not compiled in */
+    FM_ERROR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < flashmask_workspace_size(...) */
+    FM_ERROR_HIP = 4                  /* a kernel launch failed */
+} fm_status_t;
+
+typedef enum { FM_FP32 = 0, FM_BF16 = 1 } fm_dtype_t;
+
+/* Static text for a status code; never NULL. */
+const char* flashmask_status_string(fm_status_t status);
+
+/* Column granularity Bt of the key-block table that flashmask_fwd and
+ * flashmask_bwd accept as `kblock_minmax` (a table from
+ * flashmask_tile_classify with block_k == flashmask_table_block()). */
+int flashmask_table_block(void);
+
+/* Tile shape (query rows x key columns) the forward (is_bwd == 0) or backward
+ * (is_bwd != 0) kernel classifies and counts in `tile_counts`, for head dim d
+ * and dtype. Returns FM_ERROR_NOT_SUPPORTED for a combination not compiled in. */
+fm_status_t flashmask_tile_shape(int is_bwd, int d, fm_dtype_t dtype,
+                                 int* block_q, int* block_k);
+
+/* Bytes of device workspace flashmask_fwd (is_bwd == 0) or flashmask_bwd
+ * (is_bwd != 0) needs for these sizes; 0 on invalid sizes. The workspace
+ * needs 256-byte alignment. */
+size_t flashmask_workspace_size(int is_bwd, int B, int H, int N, int d, int dv,
+                                int hm, fm_dtype_t dtype);
+
+/*
+ * Key-block table and tile classes.
+ *
+ * kblock_minmax (out, int32 [B, hm, ceil(N/block_k), 8]): for every block of
+ * block_k key columns [c0, c1), c1 = min(N, c0 + block_k), the min and max of
+ * each vector in the order LTS min, LTS max, LTE min, LTE max, UTS min,
+ * UTS max, UTE min, UTE max. Missing vectors take neutral values: no lower
+ * interval -> LTS = LTE = N; lte NULL -> LTE = N; no upper interval (or
+ * uts/ute NULL) -> UTS = UTE = 0. The table depends on the vectors only.
+ *
+ * tile_class (out, nullable, int8 [B, hm, ceil(N/block_q), ceil(N/block_k)]):
+ * for rows [r0, r1) and columns [c0, c1), both clipped to N:
+ *   0 (masked, skipped): (causal && c0 > r1 - 1) || (LTSmax <= r0 && LTEmin >= r1)
+ *                        || (!causal && UTSmax <= r0 && UTEmin >= r1)
+ *   2 (unmasked):        (!causal || c1 - 1 <= r0) && (LTEmax <= r0 || LTSmin >= r1)
+ *                        && (causal || UTEmax <= r0 || UTSmin >= r1)
+ *   1 (partial):         otherwise.
+ * Conservative: a 0 or 2 is always exact, a 1 may be a tile without or with
+ * only masked elements. The skipping rule follows the FlashMask README
+ * ("Overview": mask sparsity skips unnecessary computation).
+ *
+ * block_q, block_k >= 1. Integer work: results are bit-exact.
+ */
+fm_status_t flashmask_tile_classify(const int32_t* lts, const int32_t* lte,
+                                    const int32_t* uts, const int32_t* ute,
+                                    int B, int hm, int N, int causal,
+                                    int block_q, int block_k,
+                                    int32_t* kblock_minmax, int8_t* tile_class,
+                                    void* stream);
+
+/*
+ * Forward. q, k [B,H,N,d]; v [B,H,N,dv]; o (out) [B,H,N,dv] in dtype;
+ * lse (out) [B,H,N] float32, natural log of sum_j exp(scale * q_i . k_j)
+ * over open keys (-inf for a fully masked row). kblock_minmax (nullable): a
+ * precomputed table at flashmask_table_block() granularity for these vectors
+ * (reused across calls when the mask is fixed); NULL computes it in the
+ * workspace. tile_counts (nullable, int64 [3], accumulated into, not
+ * cleared): tiles of flashmask_tile_shape(0, ...) classified masked, partial
+ * and unmasked. The output is bitwise deterministic.
+ */
+fm_status_t flashmask_fwd(const void* q, const void* k, const void* v,
+                          const int32_t* lts, const int32_t* lte,
+                          const int32_t* uts, const int32_t* ute, int hm,
+                          const int32_t* kblock_minmax,
+                          int B, int H, int N, int d, int dv, fm_dtype_t dtype,
+                          int causal, float softmax_scale,
+                          void* o, float* lse, int64_t* tile_counts,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward. Given o and lse from flashmask_fwd with the same inputs and
+ * dout [B,H,N,dv], writes dq, dk [B,H,N,d] and dv_out [B,H,N,dv] in dtype:
+ * the analytic gradient of O = softmax(scale Q K^T + M) V,
+ *   dV = P^T dO, dS = P * (dO V^T - rowsum(dO * O)), dQ = scale dS K,
+ *   dK = scale dS^T Q.
+ * tile_counts as in the forward, for flashmask_tile_shape(1, ...). dq is
+ * accumulated with float32 atomics, so its bits may vary between runs
+ * (within rounding); dk and dv_out are deterministic.
+ */
+fm_status_t flashmask_bwd(const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* dout,
+                          const int32_t* lts, const int32_t* lte,
+                          const int32_t* uts, const int32_t* ute, int hm,
+                          const int32_t* kblock_minmax,
+                          int B, int H, int N, int d, int dv, fm_dtype_t dtype,
+                          int causal, float softmax_scale,
+                          void* dq, void* dk, void* dv_out, int64_t* tile_counts,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHMASK_H */

@@ -73,29 +73,33 @@ def kblock_minmax(B, hm, n, block, lts=None, lte=None, uts=None, ute=None):
 def classify(table, n, block_q, block_k, causal):
     """int8 [B, Hm, ceil(N/block_q), ceil(N/block_k)] tile classes.
 
-    ``table`` must be the kblock_minmax table at granularity block_k.
+    ``table`` must be the kblock_minmax table at granularity block_k. The rule
+    of the module docstring is evaluated for every (query block, key block)
+    pair at once with numpy broadcasting: rows index query blocks, columns key
+    blocks.
     """
     t = np.asarray(table, np.int64)
     B, hm, nkb, _ = t.shape
     nqb = (n + block_q - 1) // block_q
+    r0 = (np.arange(nqb, dtype=np.int64) * block_q)[:, None]
+    r1 = np.minimum(n, r0 + block_q)
+    c0 = (np.arange(nkb, dtype=np.int64) * block_k)[None, :]
+    c1 = np.minimum(n, c0 + block_k)
     out = np.zeros((B, hm, nqb, nkb), np.int8)
     for b in range(B):
         for h in range(hm):
-            for qb in range(nqb):
-                r0, r1 = qb * block_q, min(n, (qb + 1) * block_q)
-                for kb in range(nkb):
-                    c0, c1 = kb * block_k, min(n, (kb + 1) * block_k)
-                    lts_mn, lts_mx, lte_mn, lte_mx, uts_mn, uts_mx, ute_mn, ute_mx = t[b, h, kb]
-                    full = (causal and c0 > r1 - 1) \
-                        or (lts_mx <= r0 and lte_mn >= r1) \
-                        or ((not causal) and uts_mx <= r0 and ute_mn >= r1)
-                    if full:
-                        out[b, h, qb, kb] = 0
-                        continue
-                    causal_free = (not causal) or (c1 - 1 <= r0)
-                    lt_free = lte_mx <= r0 or lts_mn >= r1
-                    ut_free = causal or ute_mx <= r0 or uts_mn >= r1
-                    out[b, h, qb, kb] = 2 if (causal_free and lt_free and ut_free) else 1
+            lts_mn, lts_mx, lte_mn, lte_mx, uts_mn, uts_mx, ute_mn, ute_mx = \
+                (t[b, h, :, e][None, :] for e in range(8))
+            full = (lts_mx <= r0) & (lte_mn >= r1)
+            if causal:
+                full |= c0 > r1 - 1
+            else:
+                full |= (uts_mx <= r0) & (ute_mn >= r1)
+            causal_free = (c1 - 1 <= r0) if causal else np.ones_like(full)
+            lt_free = (lte_mx <= r0) | (lts_mn >= r1)
+            ut_free = np.ones_like(full) if causal else ((ute_mx <= r0) | (uts_mn >= r1))
+            none = causal_free & lt_free & ut_free
+            out[b, h] = np.where(full, 0, np.where(none, 2, 1))
     return out
 
 

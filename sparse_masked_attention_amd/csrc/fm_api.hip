@@ -1,0 +1,232 @@
+// C ABI: argument checks, workspace layout and dispatch. Declarations and the
+// contract of every entry point are in include/flashmask.h.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/flashmask.h"
+#include "fm_internal.hpp"
+
+namespace {
+
+using fm::kTableBlock;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+bool supported(int d, int dv, fm_dtype_t dtype) {
+  if (d != dv) return false;
+  if (dtype == FM_BF16) return d == 64 || d == 128 || d == 256;
+  if (dtype == FM_FP32) return d == 64 || d == 128;
+  return false;
+}
+
+// Backward kernels compiled so far: bf16 with d = dv in {64, 128}.
+bool bwd_supported(int d, int dv, fm_dtype_t dtype) {
+  return d == dv && dtype == FM_BF16 && (d == 64 || d == 128);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t table_bytes(int B, int hm, int N) {
+  return (size_t)B * hm * (size_t)ceil_div(N, kTableBlock) * 8 * sizeof(int32_t);
+}
+
+// Checks shared by the attention entry points; FM_SUCCESS when usable.
+fm_status_t check_common(int B, int H, int N, int d, int dv, fm_dtype_t dtype, int hm,
+                         const int32_t* lts, const int32_t* lte, const int32_t* uts,
+                         const int32_t* ute, int causal) {
+  if (B < 0 || H < 0 || N < 0 || d <= 0 || dv <= 0 || hm < 1) return FM_ERROR_INVALID_VALUE;
+  if (dtype != FM_BF16 && dtype != FM_FP32) return FM_ERROR_INVALID_VALUE;
+  if (H > 0 && hm != 1 && hm != H) return FM_ERROR_INVALID_VALUE;
+  if (!causal && ((uts == nullptr) != (ute == nullptr))) return FM_ERROR_INVALID_VALUE;
+  (void)lts;
+  (void)lte;
+  if (!supported(d, dv, dtype)) return FM_ERROR_NOT_SUPPORTED;
+  // 32-bit buffer offsets address one (batch, head) slice of a tensor
+  if ((long long)N * d * (dtype == FM_BF16 ? 2 : 4) >= (1LL << 31)) return FM_ERROR_NOT_SUPPORTED;
+  if ((long long)B * H * ceil_div(N, fm::kFwdBlockQ) >= (1LL << 31)) return FM_ERROR_NOT_SUPPORTED;
+  return FM_SUCCESS;
+}
+
+fm::MaskArgs mask_args(const int32_t* lts, const int32_t* lte, const int32_t* uts,
+                       const int32_t* ute, int hm, int causal) {
+  fm::MaskArgs m;
+  m.lts = lts;
+  m.lte = lts != nullptr ? lte : nullptr;
+  const bool ut = !causal && uts != nullptr && ute != nullptr;
+  m.uts = ut ? uts : nullptr;
+  m.ute = ut ? ute : nullptr;
+  m.hm = hm;
+  m.causal = causal != 0;
+  return m;
+}
+
+float resolve_scale(float s, int d) {
+  if (!(s > 0.f)) return 1.0f / std::sqrt((float)d);  // also catches NaN
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flashmask_status_string(fm_status_t status) {
+  switch (status) {
+    case FM_SUCCESS: return "success";
+    case FM_ERROR_INVALID_VALUE: return "invalid argument";
+    case FM_ERROR_NOT_SUPPORTED: return "head dim / dtype combination not supported";
+    case FM_ERROR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FM_ERROR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int flashmask_table_block(void) { return kTableBlock; }
+
+fm_status_t flashmask_tile_shape(int is_bwd, int d, fm_dtype_t dtype, int* block_q, int* block_k) {
+  if (block_q == nullptr || block_k == nullptr) return FM_ERROR_INVALID_VALUE;
+  if (!supported(d, d, dtype)) return FM_ERROR_NOT_SUPPORTED;
+  *block_q = is_bwd ? fm::kBwdBlockQ : fm::kFwdBlockQ;
+  *block_k = is_bwd ? fm::kBwdBlockK : fm::kFwdBlockK;
+  return FM_SUCCESS;
+}
+
+size_t flashmask_workspace_size(int is_bwd, int B, int H, int N, int d, int dv, int hm,
+                                fm_dtype_t dtype) {
+  if (B < 0 || H < 0 || N < 0 || hm <= 0 || d <= 0 || dv <= 0) return 0;
+  if (!supported(d, dv, dtype)) return 0;
+  size_t bytes = align_up(table_bytes(B, hm, N));
+  if (is_bwd) {
+    bytes += align_up((size_t)B * H * N * sizeof(float));                 // delta
+    bytes += align_up((size_t)B * H * N * (size_t)d * sizeof(float));     // dQ accumulator
+  }
+  return bytes;
+}
+
+fm_status_t flashmask_tile_classify(const int32_t* lts, const int32_t* lte, const int32_t* uts,
+                                    const int32_t* ute, int B, int hm, int N, int causal,
+                                    int block_q, int block_k, int32_t* kblock_minmax,
+                                    int8_t* tile_class, void* stream) {
+  if (B < 0 || hm <= 0 || N < 0 || block_q < 1 || block_k < 1) return FM_ERROR_INVALID_VALUE;
+  if (!causal && ((uts == nullptr) != (ute == nullptr))) return FM_ERROR_INVALID_VALUE;
+  if ((long long)B * hm * N == 0) return FM_SUCCESS;
+  if (kblock_minmax == nullptr || !aligned(kblock_minmax, 16)) return FM_ERROR_INVALID_VALUE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const fm::MaskArgs m = mask_args(lts, lte, uts, ute, hm, causal);
+  if (fm::launch_kblock_minmax(m, B, N, block_k, kblock_minmax, s) != hipSuccess) return FM_ERROR_HIP;
+  if (tile_class != nullptr) {
+    if (fm::launch_classify(kblock_minmax, B, hm, N, causal != 0, block_q, block_k, tile_class, s) !=
+        hipSuccess)
+      return FM_ERROR_HIP;
+  }
+  return FM_SUCCESS;
+}
+
+fm_status_t flashmask_fwd(const void* q, const void* k, const void* v, const int32_t* lts,
+                          const int32_t* lte, const int32_t* uts, const int32_t* ute, int hm,
+                          const int32_t* kblock_minmax, int B, int H, int N, int d, int dv,
+                          fm_dtype_t dtype, int causal, float softmax_scale, void* o, float* lse,
+                          int64_t* tile_counts, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  fm_status_t st = check_common(B, H, N, d, dv, dtype, hm, lts, lte, uts, ute, causal);
+  if (st != FM_SUCCESS) return st;
+  if ((long long)B * H * N == 0) return FM_SUCCESS;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr)
+    return FM_ERROR_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return FM_ERROR_INVALID_VALUE;
+  if (kblock_minmax != nullptr && !aligned(kblock_minmax, 16)) return FM_ERROR_INVALID_VALUE;
+  const size_t need = flashmask_workspace_size(0, B, H, N, d, dv, hm, dtype);
+  if (kblock_minmax == nullptr && (workspace == nullptr || workspace_bytes < need))
+    return FM_ERROR_WORKSPACE_TOO_SMALL;
+  if (workspace != nullptr && !aligned(workspace, kAlign)) return FM_ERROR_INVALID_VALUE;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  fm::AttnArgs a{};
+  a.mask = mask_args(lts, lte, uts, ute, hm, causal);
+  const int32_t* table = kblock_minmax;
+  if (table == nullptr) {
+    int32_t* t = reinterpret_cast<int32_t*>(workspace);
+    if (fm::launch_kblock_minmax(a.mask, B, N, kTableBlock, t, s) != hipSuccess) return FM_ERROR_HIP;
+    table = t;
+  }
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.table = table;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.dv = dv;
+  a.is_bf16 = dtype == FM_BF16;
+  a.scale = resolve_scale(softmax_scale, d);
+  a.out = o;
+  a.lse_out = lse;
+  a.tile_counts = reinterpret_cast<unsigned long long*>(tile_counts);
+  if (fm::launch_fwd(a, s) != hipSuccess) return FM_ERROR_HIP;
+  return FM_SUCCESS;
+}
+
+fm_status_t flashmask_bwd(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, const int32_t* lts,
+                          const int32_t* lte, const int32_t* uts, const int32_t* ute, int hm,
+                          const int32_t* kblock_minmax, int B, int H, int N, int d, int dv,
+                          fm_dtype_t dtype, int causal, float softmax_scale, void* dq, void* dk,
+                          void* dv_out, int64_t* tile_counts, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  fm_status_t st = check_common(B, H, N, d, dv, dtype, hm, lts, lte, uts, ute, causal);
+  if (st != FM_SUCCESS) return st;
+  if (!bwd_supported(d, dv, dtype)) return FM_ERROR_NOT_SUPPORTED;
+  if ((long long)B * H * N == 0) return FM_SUCCESS;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
+      dout == nullptr || dq == nullptr || dk == nullptr || dv_out == nullptr)
+    return FM_ERROR_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv_out, 16))
+    return FM_ERROR_INVALID_VALUE;
+  if (kblock_minmax != nullptr && !aligned(kblock_minmax, 16)) return FM_ERROR_INVALID_VALUE;
+  const size_t need = flashmask_workspace_size(1, B, H, N, d, dv, hm, dtype);
+  if (workspace == nullptr || workspace_bytes < need) return FM_ERROR_WORKSPACE_TOO_SMALL;
+  if (!aligned(workspace, kAlign)) return FM_ERROR_INVALID_VALUE;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  fm::AttnArgs a{};
+  a.mask = mask_args(lts, lte, uts, ute, hm, causal);
+  const int32_t* table = kblock_minmax;
+  if (table == nullptr) {
+    int32_t* t = reinterpret_cast<int32_t*>(ws);
+    if (fm::launch_kblock_minmax(a.mask, B, N, kTableBlock, t, s) != hipSuccess) return FM_ERROR_HIP;
+    table = t;
+  }
+  ws += align_up(table_bytes(B, hm, N));
+  a.delta = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)B * H * N * sizeof(float));
+  a.dq_acc = reinterpret_cast<float*>(ws);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.table = table;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.dv = dv;
+  a.is_bf16 = dtype == FM_BF16;
+  a.scale = resolve_scale(softmax_scale, d);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv_out = dv_out;
+  a.tile_counts = reinterpret_cast<unsigned long long*>(tile_counts);
+  if (fm::launch_bwd(a, s) != hipSuccess) return FM_ERROR_HIP;
+  return FM_SUCCESS;
+}
+
+}  // extern "C"

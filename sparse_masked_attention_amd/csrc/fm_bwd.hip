@@ -1,0 +1,545 @@
+// Backward kernels: dQ, dK, dV of O = softmax(scale * Q K^T + M) V.
+//
+// The pages give the forward (FlashMask README "Formulation") and say FlashMask
+// ships forward and backward kernels (README "Overview"). The gradient is the
+// analytic one of that expression, recomputing the probabilities from the
+// saved logsumexp so nothing of size N x N is stored (the FlashMask abstract
+// credits FlashAttention with removing that O(N^2) memory):
+//   P = exp(scale * Q K^T - LSE) on open pairs, dV = P^T dO,
+//   dS = P * (dO V^T - delta), delta_i = sum_m dO[i][m] * O[i][m],
+//   dQ = scale * dS K, dK = scale * dS^T Q.
+//
+// gfx950 mapping (bf16 path, d = dv in {64, 128}):
+//   * A workgroup (4 waves) owns 128 keys, 32 per wave; K and V of those keys
+//     stay in registers as MFMA operands, dK and dV accumulate in registers.
+//   * It walks the query blocks (64 rows) the mask leaves visible, found by
+//     the same per-block min/max classification as the forward, with a
+//     per-wave class so a wave whose 32 keys are hidden does no math.
+//   * Q and dO tiles (plus LSE and delta) arrive by buffer loads straight into
+//     LDS, double buffered. P and dS are formed in the S = Q K^T accumulator
+//     layout, which is directly the A operand of dV += P^T dO and
+//     dK += dS^T Q; the Q/dO operands come from ds_read_b64_tr_b16.
+//   * dS^T goes to LDS once per step; each wave then forms a quarter of the
+//     step's dQ (64 rows x d) over all 128 keys and adds it into a float32
+//     accumulator with global atomics. A last kernel converts it to bf16.
+//   * Because each lane owns one key, the element mask test of a partial tile
+//     uses four per-lane registers (that key's bounds) and no memory.
+#include <type_traits>
+
+#include "fm_device.hpp"
+#include "fm_internal.hpp"
+
+namespace fm {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  const int32_t* lts;
+  const int32_t* lte;
+  const int32_t* uts;
+  const int32_t* ute;
+  const int32_t* table;  // [B, hm, ceil(N/64), 8]
+  float* dq_acc;
+  float* delta;
+  void* dq;
+  void* dk;
+  void* dv;
+  unsigned long long* counts;
+  int B, H, N, hm, causal;
+  int has_lt, has_lte, has_ut;
+  float scale, sl2;
+  int nqb, nkb, nkb64;
+};
+
+// ---------------------------------------------------------------- preprocess
+// delta_i = sum_m dO[i][m] * O[i][m] in float32, and zero the dQ accumulator
+// rows. 16 threads per row; each handles 16-byte chunks.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+  const long long rows = (long long)p.B * p.H * p.N;
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int t = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+    const T* dog = reinterpret_cast<const T*>(p.dout) + row * D;
+    const T* og = reinterpret_cast<const T*>(p.o) + row * D;
+#pragma unroll
+    for (int c = t; c < D / EPC; c += 16) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(dog + c * EPC);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(og + c * EPC);
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 x = __builtin_bit_cast(bf16x8, a), y = __builtin_bit_cast(bf16x8, b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += (float)x[e] * (float)y[e];
+      } else {
+        const f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += x[e] * y[e];
+      }
+    }
+    float* dqa = p.dq_acc + row * D;
+#pragma unroll
+    for (int c = t; c < D / 4; c += 16) *reinterpret_cast<f32x4*>(dqa + 4 * c) = f32x4{};
+  }
+#pragma unroll
+  for (int s = 8; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 16);
+  if (row < rows && t == 0) p.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------- dQ convert
+template <typename T>
+__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ src, T* __restrict__ dst,
+                                                         long long n4) {
+  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < n4;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(src)[idx];
+    if constexpr (sizeof(T) == 2) {
+      bf16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+      reinterpret_cast<bf16x4*>(dst)[idx] = o;
+    } else {
+      reinterpret_cast<f32x4*>(dst)[idx] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- main kernel
+template <int D>
+struct BwdCfg {
+  static constexpr int NW = 4;
+  static constexpr int KW = 32;                 // keys per wave
+  static constexpr int BKC = NW * KW;           // keys per workgroup
+  static constexpr int BQ = 64;                 // query rows per step
+  static constexpr int CH = D / 8;
+  static constexpr int QT = BQ * D * 2;         // bytes of one Q or dO tile
+  static constexpr int LOADS = QT / (NW * 1024);
+  static constexpr int STAGE = 2 * QT + 2 * BQ * 4;  // Q, dO, LSE, delta
+  static constexpr int KT = BKC * D * 2;        // resident K tile (dQ operand)
+  static constexpr int KLOADS = KT / (NW * 1024);
+  static constexpr int DSS = BQ + 8;            // dS^T row stride (bf16), padded
+  static constexpr int DS = BKC * DSS * 2;
+  static constexpr int LIST = 1024;
+  static constexpr int LOADS_PER_STEP = 2 * LOADS + 1;   // per wave (wave 0/1 add lse/delta)
+};
+
+// Chunk swizzle shared by row reads (32 rows, one chunk) and transposed reads
+// (8 rows x 4 chunks) of the Q, dO and K tiles.
+template <int D>
+__device__ inline int swz(int row) {
+  if constexpr (D >= 128) return 4 * (row & 3) + ((row >> 2) & 3);
+  else return 4 * (row & 1) + ((row >> 1) & 3);
+}
+
+template <int D>
+__device__ inline const FM_LDS char* tile_addr(const FM_LDS char* base, int row, int col) {
+  // byte address of element (row, col) of a swizzled row-major bf16 tile
+  return base + row * D * 2 + (((col >> 3) ^ swz<D>(row)) << 4) + (col & 7) * 2;
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
+  using C = BwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char ktile[C::KT];
+  __shared__ __attribute__((aligned(16))) bf16 dsT[C::BKC * C::DSS];
+  __shared__ int list[C::LIST];
+  __shared__ int wsum[C::NW];
+  __shared__ unsigned wcount[3];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;
+  const int kb = (int)(blockIdx.x / BH);     // heavy (early) key blocks first
+  const int b = bh / p.H, h = bh % p.H;
+  const int hmi = p.hm == 1 ? 0 : h;
+  const int N = p.N;
+  const long long slice = (long long)bh * N;
+  const int c0 = kb * C::BKC;
+  const int c1 = min(N, c0 + C::BKC);
+  const int wc0 = c0 + C::KW * w;                // this wave's first key
+  const int j = wc0 + l32;                        // this lane's key
+  const uint32_t tbytes = (uint32_t)N * D * 2;
+
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(p.q) + slice * D, tbytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + slice * D, tbytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + slice * D, tbytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const bf16*>(p.dout) + slice * D, tbytes);
+  const __amdgpu_buffer_rsrc_t rlse = make_rsrc(p.lse + slice, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t rdel = make_rsrc(p.delta + slice, (uint32_t)N * 4);
+
+  // K tile of the workgroup's keys into LDS (dQ operand), rows past N zero
+#pragma unroll
+  for (int u = 0; u < C::KLOADS; ++u) {
+    const int g = (w * C::KLOADS + u) * 64 + lane;
+    const int row = g / C::CH, pch = g % C::CH;
+    load_lds16(rk, (FM_LDS char*)ktile + (w * C::KLOADS + u) * 1024,
+               (uint32_t)((c0 + row) * D + 8 * (pch ^ swz<D>(row))) * 2);
+  }
+  // K and V of this lane's key as the B operands of S = Q K^T and dP = dO V^T
+  bf16x8 kB[D / 16], vB[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    kB[c] = __builtin_bit_cast(bf16x8, buffer_load16(rk, (uint32_t)(j * D + 16 * c + 8 * hh) * 2));
+    vB[c] = __builtin_bit_cast(bf16x8, buffer_load16(rv, (uint32_t)(j * D + 16 * c + 8 * hh) * 2));
+  }
+  // this lane's key bounds (the element test needs nothing else)
+  const long long vrow = ((long long)b * p.hm + hmi) * N;
+  int k_lts = N, k_lte = N, k_uts = 0, k_ute = 0;
+  if (j < N) {
+    if (p.has_lt) {
+      k_lts = p.lts[vrow + j];
+      k_lte = p.has_lte ? p.lte[vrow + j] : N;
+    }
+    if (p.has_ut) {
+      k_uts = p.uts[vrow + j];
+      k_ute = p.ute[vrow + j];
+    }
+  }
+
+  f32x16 dvacc[D / 32], dkacc[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+    dvacc[mb] = f32x16{};
+    dkacc[mb] = f32x16{};
+  }
+  if (tid < 3) wcount[tid] = 0;
+  unsigned cnt0 = 0, cnt1 = 0, cnt2 = 0;
+  const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb64 * 8;
+
+  auto issue = [&](unsigned entry, auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
+    FM_LDS char* st = (FM_LDS char*)(S ? stage1 : stage0);
+    const int q0 = (int)(entry & 0xFFFFFFu) * C::BQ;
+#pragma unroll
+    for (int u = 0; u < C::LOADS; ++u) {
+      const int g = (w * C::LOADS + u) * 64 + lane;
+      const int row = g / C::CH, pch = g % C::CH;
+      const uint32_t off = (uint32_t)((q0 + row) * D + 8 * (pch ^ swz<D>(row))) * 2;
+      load_lds16(rq, st + (w * C::LOADS + u) * 1024, off);
+      load_lds16(rdo, st + C::QT + (w * C::LOADS + u) * 1024, off);
+    }
+    // 64 LSE values then 64 delta values: 16 lanes x 16 bytes each
+    if (w < 2 && lane < 16)
+      load_lds16(w == 0 ? rlse : rdel, st + 2 * C::QT + w * 256, (uint32_t)(q0 + 4 * lane) * 4);
+  };
+
+  auto compute = [&](unsigned entry, auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
+    const FM_LDS char* qst = (const FM_LDS char*)(S ? stage1 : stage0);
+    const FM_LDS char* dost = qst + C::QT;
+    const FM_LDS float* lse_l = (const FM_LDS float*)(qst + 2 * C::QT);
+    const FM_LDS float* del_l = lse_l + C::BQ;
+    const int q0 = (int)(entry & 0xFFFFFFu) * C::BQ;
+    const int wc = (int)((entry >> (24 + 2 * w)) & 3u);
+    bf16x8 pB[C::BQ / 16], dsB[C::BQ / 16];
+    if (wc != 0) {
+      f32x16 sacc[C::BQ / 32], dpacc[C::BQ / 32];
+#pragma unroll
+      for (int ib = 0; ib < C::BQ / 32; ++ib) {
+        sacc[ib] = f32x16{};
+        dpacc[ib] = f32x16{};
+        const int row = 32 * ib + l32;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          const bf16x8 a = lds_read_b128(tile_addr<D>(qst, row, 16 * c + 8 * hh));
+          sacc[ib] = mfma32(a, kB[c], sacc[ib]);
+        }
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          const bf16x8 a = lds_read_b128(tile_addr<D>(dost, row, 16 * c + 8 * hh));
+          dpacc[ib] = mfma32(a, vB[c], dpacc[ib]);
+        }
+      }
+#pragma unroll
+      for (int ib = 0; ib < C::BQ / 32; ++ib) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int rl = 32 * ib + 8 * g + 4 * hh;   // first of 4 rows held
+          const f32x4 lse4 = *reinterpret_cast<const FM_LDS f32x4*>(lse_l + rl);
+          const f32x4 del4 = *reinterpret_cast<const FM_LDS f32x4*>(del_l + rl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const int i = q0 + rl + e;
+            float s = sacc[ib][r];
+            if (wc == 1) {
+              bool m = (i >= N) || (j >= N) || (p.causal && j > i);
+              m = m || (k_lts <= i && i < k_lte) || (k_uts <= i && i < k_ute);
+              if (m) s = kNegInf;
+            }
+            // fully masked rows have LSE = -inf: their P is 0
+            const float l2 = lse4[e] == kNegInf ? __builtin_inff() : lse4[e] * kLog2e;
+            const float pv = fast_exp2(__builtin_fmaf(s, p.sl2, -l2));
+            const float ds = pv * (dpacc[ib][r] - del4[e]) * p.scale;
+            pB[2 * ib + r / 8][r % 8] = (bf16)pv;
+            dsB[2 * ib + r / 8][r % 8] = (bf16)ds;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < C::BQ / 16; ++c) {
+        pB[c] = bf16x8{};
+        dsB[c] = bf16x8{};
+      }
+    }
+    // dS^T to LDS: row = key (this lane's), 4 consecutive query rows per store
+    {
+      bf16* row_ptr = dsT + (C::KW * w + l32) * C::DSS;
+#pragma unroll
+      for (int c = 0; c < C::BQ / 16; ++c) {
+        // chunk c holds rows 16c + 4h + 0..3 (elements 0..3) and 16c + 8 + 4h + 0..3
+        const bf16x4 lo = __builtin_shufflevector(dsB[c], dsB[c], 0, 1, 2, 3);
+        const bf16x4 hi = __builtin_shufflevector(dsB[c], dsB[c], 4, 5, 6, 7);
+        *reinterpret_cast<FM_LDS bf16x4*>((FM_LDS bf16*)row_ptr + 16 * c + 4 * hh) = lo;
+        *reinterpret_cast<FM_LDS bf16x4*>((FM_LDS bf16*)row_ptr + 16 * c + 8 + 4 * hh) = hi;
+      }
+    }
+    if (wc != 0) {
+      // dV += P^T dO and dK += dS^T Q; dO / Q operands by transposed reads
+      const int sl = lane & 15;
+#pragma unroll
+      for (int c = 0; c < C::BQ / 16; ++c) {
+        const int ra = 16 * c + 4 * hh + (sl >> 2);
+        const int rb = ra + 8;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb) {
+          const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+          const bf16x8 bo = cat(lds_read_tr(tile_addr<D>(dost, ra, col)), lds_read_tr(tile_addr<D>(dost, rb, col)));
+          dvacc[mb] = mfma32(pB[c], bo, dvacc[mb]);
+          const bf16x8 bq = cat(lds_read_tr(tile_addr<D>(qst, ra, col)), lds_read_tr(tile_addr<D>(qst, rb, col)));
+          dkacc[mb] = mfma32(dsB[c], bq, dkacc[mb]);
+        }
+      }
+    }
+    lds_barrier();
+    // dQ over all 128 keys: the step's (BQ/32) x (D/32) output blocks of 32x32
+    // are split evenly over the waves; a wave's blocks share one row block.
+    {
+      constexpr int BPW = (C::BQ / 32) * (D / 32) / C::NW;
+      const int ob0 = w * BPW;
+      const int ib = ob0 / (D / 32);
+      const int sl = lane & 15;
+      f32x16 dq[BPW];
+#pragma unroll
+      for (int t = 0; t < BPW; ++t) dq[t] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < C::BKC / 16; ++c) {
+        // A: dS[i][16c + 8h + e] from dS^T (row = key, column = query)
+        const int kr = 16 * c + 8 * hh + (sl >> 2);
+        const int qcol = 32 * ib + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+        const FM_LDS bf16* d0 = (const FM_LDS bf16*)dsT + kr * C::DSS + qcol;
+        const bf16x8 a = cat(lds_read_tr(d0), lds_read_tr(d0 + 4 * C::DSS));
+#pragma unroll
+        for (int t = 0; t < BPW; ++t) {
+          const int mb = (ob0 + t) % (D / 32);
+          const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+          const bf16x8 bk = cat(lds_read_tr(tile_addr<D>((const FM_LDS char*)ktile, kr, col)),
+                                lds_read_tr(tile_addr<D>((const FM_LDS char*)ktile, kr + 4, col)));
+          dq[t] = mfma32(a, bk, dq[t]);
+        }
+      }
+      // add into the float32 accumulator (lane holds column 32mb + lane % 32)
+#pragma unroll
+      for (int t = 0; t < BPW; ++t) {
+        const int mb = (ob0 + t) % (D / 32);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = q0 + 32 * ib + 8 * (r / 4) + 4 * hh + (r % 4);
+          if (i < N) unsafeAtomicAdd(p.dq_acc + (slice + i) * D + 32 * mb + l32, dq[t][r]);
+        }
+      }
+    }
+  };
+
+  // --- scan query blocks, compact the visible ones, process in chunks
+  const bool tail = c1 - c0 < C::BKC;
+  BlockBounds kbnd;
+  {
+    const BlockBounds a = load_bounds(table + (long long)(c0 / 64) * 8);
+    BlockBounds m = a;
+    if (c0 / 64 + 1 < p.nkb64) {
+      const BlockBounds q = load_bounds(table + (long long)(c0 / 64 + 1) * 8);
+      m.lts_mn = min(a.lts_mn, q.lts_mn); m.lts_mx = max(a.lts_mx, q.lts_mx);
+      m.lte_mn = min(a.lte_mn, q.lte_mn); m.lte_mx = max(a.lte_mx, q.lte_mx);
+      m.uts_mn = min(a.uts_mn, q.uts_mn); m.uts_mx = max(a.uts_mx, q.uts_mx);
+      m.ute_mn = min(a.ute_mn, q.ute_mn); m.ute_mx = max(a.ute_mx, q.ute_mx);
+    }
+    kbnd = m;
+  }
+  int cnt = 0;
+  for (int base = 0; base < p.nqb; base += 256) {
+    const int qb = base + tid;
+    unsigned entry = 0;
+    bool valid = false;
+    if (qb < p.nqb) {
+      const int r0 = qb * C::BQ, r1 = min(N, r0 + C::BQ);
+      const int wgc = tile_class(kbnd, r0, r1, c0, c1, p.causal != 0);
+      cnt0 += wgc == 0;
+      cnt1 += wgc == 1;
+      cnt2 += wgc == 2;
+      if (wgc != 0) {
+        valid = true;
+        const bool ragged = tail || (r1 - r0 < C::BQ);
+        int bits = 0;
+#pragma unroll
+        for (int ww = 0; ww < C::NW; ++ww) {
+          const int a0 = c0 + C::KW * ww;
+          int cls = 0;
+          if (a0 < N) {
+            const BlockBounds wb = load_bounds(table + (long long)(a0 / 64) * 8);
+            cls = tile_class(wb, r0, r1, a0, min(N, a0 + C::KW), p.causal != 0);
+            if (ragged && cls == 2) cls = 1;
+          }
+          bits |= cls << (2 * ww);
+        }
+        entry = (unsigned)qb | ((unsigned)bits << 24);
+      }
+    }
+    const unsigned long long bal = __ballot(valid);
+    const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+    if (lane == 0) wsum[w] = __builtin_popcountll(bal);
+    __syncthreads();
+    int off = cnt, add = 0;
+#pragma unroll
+    for (int ww = 0; ww < C::NW; ++ww) {
+      const int v = wsum[ww];
+      if (ww < w) off += v;
+      add += v;
+    }
+    if (valid) list[off + rank] = (int)entry;
+    __syncthreads();
+    cnt += add;
+    if (cnt > C::LIST - 256 || base + 256 >= p.nqb) {
+      auto step = [&](int it, auto stage_c) {
+        constexpr int S = decltype(stage_c)::value;
+        const unsigned entry_it = (unsigned)list[it];
+        if (it + 1 < cnt) {
+          issue((unsigned)list[it + 1], std::integral_constant<int, 1 - S>{});
+          // waves 0 and 1 issued one more load (LSE / delta)
+          if (w < 2) wait_vmcnt<C::LOADS_PER_STEP>();
+          else wait_vmcnt<C::LOADS_PER_STEP - 1>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        lds_barrier();
+        compute(entry_it, stage_c);
+        lds_barrier();
+      };
+      if (cnt > 0) issue((unsigned)list[0], std::integral_constant<int, 0>{});
+      for (int it = 0; it < cnt; it += 2) {
+        step(it, std::integral_constant<int, 0>{});
+        if (it + 1 < cnt) step(it + 1, std::integral_constant<int, 1>{});
+      }
+      cnt = 0;
+    }
+  }
+
+  wait_vmcnt<0>();  // no load into LDS may still be in flight when the wave ends
+  // --- write dK (already scaled) and dV for this wave's keys
+  if (wc0 < N) {
+    bf16* dkg = reinterpret_cast<bf16*>(p.dk) + slice * D;
+    bf16* dvg = reinterpret_cast<bf16*>(p.dv) + slice * D;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = wc0 + 8 * (r / 4) + 4 * hh + (r % 4);
+        if (key < N) {
+          dkg[(long long)key * D + 32 * mb + l32] = (bf16)dkacc[mb][r];
+          dvg[(long long)key * D + 32 * mb + l32] = (bf16)dvacc[mb][r];
+        }
+      }
+  }
+  if (p.counts != nullptr) {
+    atomicAdd(&wcount[0], cnt0);
+    atomicAdd(&wcount[1], cnt1);
+    atomicAdd(&wcount[2], cnt2);
+    __syncthreads();
+    if (tid < 3) atomicAdd(p.counts + tid, (unsigned long long)wcount[tid]);
+  }
+}
+
+// ---------------------------------------------------------------- launch
+template <int D, typename T>
+static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
+  const long long rows = (long long)p.B * p.H * p.N;
+  const long long blocks = (rows + 15) / 16;
+  hipLaunchKernelGGL((bwd_pre_kernel<D, T>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_convert(const BwdParams& p, int d, hipStream_t stream) {
+  const long long n4 = (long long)p.B * p.H * p.N * d / 4;
+  long long blocks = (n4 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL((dq_convert_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, stream, p.dq_acc,
+                     reinterpret_cast<T*>(p.dq), n4);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+  hipError_t e = launch_pre<D, bf16>(p, stream);
+  if (e != hipSuccess) return e;
+  const long long grid = (long long)p.B * p.H * p.nkb;
+  hipLaunchKernelGGL(bwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_convert<bf16>(p, D, stream);
+}
+
+hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
+  BwdParams p{};
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.dout = a.dout;
+  p.lts = a.mask.lts;
+  p.lte = a.mask.lte;
+  p.uts = a.mask.uts;
+  p.ute = a.mask.ute;
+  p.table = a.table;
+  p.dq_acc = a.dq_acc;
+  p.delta = a.delta;
+  p.dq = a.dq;
+  p.dk = a.dk;
+  p.dv = a.dv_out;
+  p.counts = a.tile_counts;
+  p.B = a.B;
+  p.H = a.H;
+  p.N = a.N;
+  p.hm = a.mask.hm;
+  p.causal = a.mask.causal;
+  p.has_lt = a.mask.lts != nullptr;
+  p.has_lte = a.mask.lts != nullptr && a.mask.lte != nullptr;
+  p.has_ut = !a.mask.causal && a.mask.uts != nullptr && a.mask.ute != nullptr;
+  p.scale = a.scale;
+  p.sl2 = a.scale * kLog2e;
+  p.nqb = (a.N + kBwdBlockQ - 1) / kBwdBlockQ;
+  p.nkb = (a.N + kBwdBlockK - 1) / kBwdBlockK;
+  p.nkb64 = (a.N + kTableBlock - 1) / kTableBlock;
+  if (a.is_bf16) {
+    switch (a.d) {
+      case 64: return launch_bwd_bf16<64>(p, stream);
+      case 128: return launch_bwd_bf16<128>(p, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fm

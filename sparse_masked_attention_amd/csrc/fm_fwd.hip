@@ -1,0 +1,528 @@
+// Forward kernels: O = softmax(scale * Q K^T + M) V and its logsumexp.
+//
+// The operation is the FlashMask README "Formulation"; M is the column-wise
+// sparse mask (README "Overview", FlashMask-3 abstract). Work is tiled the
+// FlashAttention way (the FlashMask abstract calls FlashMask an extension of
+// it): each workgroup owns a block of query rows, streams key/value tiles
+// through LDS and keeps a running row max and row sum (online softmax), so
+// nothing of size N x N exists. Tiles the per-key-block table proves hidden
+// are never loaded; tiles it proves untouched run without mask arithmetic.
+//
+// gfx950 mapping (bf16 path):
+//   * 4 waves x 32 query rows = 128 rows per workgroup; key tiles of 64.
+//   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//     each lane then owns one query row (its column of S^T) and 32 of the 64
+//     keys, so the row max needs one cross-half exchange and the row sum none
+//     until the end, and the probabilities are already laid out as the B
+//     operand of O^T += V^T P^T (the MFMA contraction index is permuted to
+//     match the accumulator layout; the same permutation is applied to V^T).
+//   * K and V tiles arrive by buffer loads straight into LDS (no VGPR
+//     staging), double buffered; out-of-range rows read as zero.
+//   * V^T operands come from the row-major V tile with ds_read_b64_tr_b16.
+//   * A workgroup first compacts the list of key tiles it must visit (with a
+//     per-wave class for each), so hidden tiles cost nothing in the loop.
+#include <type_traits>
+
+#include "fm_device.hpp"
+#include "fm_internal.hpp"
+
+namespace fm {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* lts;
+  const int32_t* lte;
+  const int32_t* uts;
+  const int32_t* ute;
+  const int32_t* table;  // [B, hm, nkb, 8] at 64-column blocks
+  void* o;
+  float* lse;
+  unsigned long long* counts;
+  int B, H, N, hm, causal;
+  int has_lt, has_lte, has_ut;
+  float scale, sl2;
+  int nqb, nkb;
+};
+
+// ---------------------------------------------------------------- shared mask test
+// Apply the element test to a 32x32 S^T block held in the MFMA accumulator
+// layout: lane (i = lane % 32, h = lane / 32), register r holds key
+// 8 * (r / 4) + 4 * h + r % 4 of the block. `vl` points at the tile's four
+// boundary vectors in LDS ([4][64] int32) and `kl0` is the block's first key
+// within the tile.
+__device__ inline void mask_block(f32x16& s, const FM_LDS int* vl, int kl0, int kbase, int i,
+                                  const FwdParams& p, int hh) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int kl = kl0 + 8 * g + 4 * hh;
+    i32x4 lts4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 0 * 64 + kl);
+    i32x4 lte4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 1 * 64 + kl);
+    i32x4 uts4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 2 * 64 + kl);
+    i32x4 ute4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 3 * 64 + kl);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = kbase + kl + e;
+      bool m = (j >= p.N) || (p.causal && j > i);
+      const int lte_v = p.has_lte ? lte4[e] : p.N;
+      m = m || (p.has_lt && lts4[e] <= i && i < lte_v);
+      m = m || (p.has_ut && uts4[e] <= i && i < ute4[e]);
+      if (m) s[4 * g + e] = kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bf16 kernel
+template <int D>
+struct FwdCfg {
+  static constexpr int NW = 4;
+  static constexpr int BR = 32 * NW;
+  static constexpr int BC = 64;
+  static constexpr int CH = D / 8;                        // 16-byte chunks per row
+  static constexpr int TILE = BC * D * 2;                 // bytes of one K or V tile
+  static constexpr int LOADS = TILE / (NW * 1024);        // per wave per tensor
+  static constexpr int VEC = 4 * BC * 4;                  // the tile's boundary vectors
+  static constexpr int STAGE = 2 * TILE + VEC;
+  static constexpr int LIST = 1024;                       // compacted tile list entries
+  static constexpr int LOADS_PER_TILE = 2 * LOADS + 1;    // per wave
+};
+
+// XOR swizzles of the 16-byte chunk index, chosen per tile so that the MFMA
+// operand reads (K: 32 rows at one chunk; V: transposed 8-row blocks) spread
+// over the LDS banks.
+template <int D>
+__device__ inline int swz_k(int row) { return row & ((D / 8 < 16 ? D / 8 : 16) - 1); }
+template <int D>
+__device__ inline int swz_v(int row) {
+  if constexpr (D == 64) return 4 * ((row >> 1) & 1);
+  else return 4 * (row & 3);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_bf16_kernel(FwdParams p) {
+  using C = FwdCfg<D>;
+  // Two pipeline stages as separate LDS objects, so the compiler can tell
+  // that reads of one stage do not depend on the loads landing in the other.
+  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
+  __shared__ int list[C::LIST];
+  __shared__ int wsum[C::NW];
+  __shared__ unsigned wcount[3];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int hh = lane >> 5;
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;
+  const int qb = p.nqb - 1 - (int)(blockIdx.x / BH);
+  const int b = bh / p.H, h = bh % p.H;
+  const int hmi = p.hm == 1 ? 0 : h;
+  const int N = p.N;
+  const long long slice = (long long)bh * N;
+  const int r0 = qb * C::BR;
+  const int r1 = min(N, r0 + C::BR);
+  const int i = r0 + 32 * w + (lane & 31);
+
+  const bf16* qg = reinterpret_cast<const bf16*>(p.q) + slice * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + slice * D, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + slice * D, (uint32_t)N * D * 2);
+  const long long vrow = ((long long)b * p.hm + hmi) * N;
+  const int32_t* vecs[4] = {p.lts, p.lte, p.uts, p.ute};
+  // each wave stages one of the four boundary vectors (absent ones read as 0)
+  const int32_t* my_vec = vecs[w];
+  const bool vec_present = my_vec != nullptr && (w < 2 ? p.has_lt : p.has_ut);
+  const __amdgpu_buffer_rsrc_t rvec =
+      make_rsrc(vec_present ? my_vec + vrow : p.table, vec_present ? (uint32_t)N * 4 : 0u);
+
+  // Q rows of this lane as the B operand of S^T = K Q^T: chunk c holds
+  // Q[i][16c + 8h .. 16c + 8h + 7]. Rows past N read as zero.
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+    qf[c] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(i * D + 16 * c + 8 * hh) * 2));
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+
+  if (tid < 3) wcount[tid] = 0;
+  unsigned cnt0 = 0, cnt1 = 0, cnt2 = 0;
+  const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb * 8;
+
+  // --- issue the loads of one key tile into a stage
+  auto issue = [&](unsigned entry, auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
+    const int kbase = (int)(entry & 0xFFFFFFu) * C::BC;
+    FM_LDS char* st = (FM_LDS char*)(S ? stage1 : stage0);
+#pragma unroll
+    for (int u = 0; u < C::LOADS; ++u) {
+      const int g = (w * C::LOADS + u) * 64 + lane;   // physical chunk in the tile
+      const int row = g / C::CH, pch = g % C::CH;
+      const uint32_t ko = (uint32_t)((kbase + row) * D + 8 * (pch ^ swz_k<D>(row))) * 2;
+      load_lds16(rk, st + (w * C::LOADS + u) * 1024, ko);
+    }
+#pragma unroll
+    for (int u = 0; u < C::LOADS; ++u) {
+      const int g = (w * C::LOADS + u) * 64 + lane;
+      const int row = g / C::CH, pch = g % C::CH;
+      const uint32_t vo = (uint32_t)((kbase + row) * D + 8 * (pch ^ swz_v<D>(row))) * 2;
+      load_lds16(rv, st + C::TILE + (w * C::LOADS + u) * 1024, vo);
+    }
+    // 16 lanes x 16 bytes = one 64-key vector per wave
+    if (lane < 16) load_lds16(rvec, st + 2 * C::TILE + w * 256, (uint32_t)(kbase + 4 * lane) * 4);
+  };
+
+  // --- one key tile of work for this wave
+  auto compute = [&](unsigned entry, auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
+    const int wc = (int)((entry >> (24 + 2 * w)) & 3u);
+    if (wc == 0) return;
+    const int kbase = (int)(entry & 0xFFFFFFu) * C::BC;
+    const FM_LDS char* kst = (const FM_LDS char*)(S ? stage1 : stage0);
+    const FM_LDS char* vst = kst + C::TILE;
+    const FM_LDS int* vl = (const FM_LDS int*)(kst + 2 * C::TILE);
+
+    f32x16 s[C::BC / 32];
+#pragma unroll
+    for (int jb = 0; jb < C::BC / 32; ++jb) {
+      s[jb] = f32x16{};
+      const int row = jb * 32 + (lane & 31);
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const bf16x8 a = lds_read_b128(kst + row * D * 2 + ((2 * c + hh) ^ swz_k<D>(row)) * 16);
+        s[jb] = mfma32(a, qf[c], s[jb]);
+      }
+    }
+    if (wc == 1) {
+#pragma unroll
+      for (int jb = 0; jb < C::BC / 32; ++jb) mask_block(s[jb], vl, jb * 32, kbase, i, p, hh);
+    }
+    // online softmax (base-2 exponent with the scale folded in)
+    float mx = kNegInf;
+#pragma unroll
+    for (int jb = 0; jb < C::BC / 32; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2((m_run - m_use) * p.sl2);
+    const float msl = m_use * p.sl2;
+    float rs = 0.f;
+    bf16x8 pf[C::BC / 16];
+#pragma unroll
+    for (int jb = 0; jb < C::BC / 32; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = fast_exp2(__builtin_fmaf(s[jb][r], p.sl2, -msl));
+        rs += pv;
+        pf[2 * jb + r / 8][r % 8] = (bf16)pv;
+      }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+    // O^T += V^T P^T; V^T chunks via transposed reads of the row-major tile
+    const int sl = lane & 15;
+#pragma unroll
+    for (int c = 0; c < C::BC / 16; ++c) {
+      const int row_a = 16 * c + 4 * hh + (sl >> 2);
+      const int row_b = row_a + 8;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) {
+        const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+        const FM_LDS char* pa = vst + row_a * D * 2 + (((col >> 3) ^ swz_v<D>(row_a)) << 4) + (col & 7) * 2;
+        const FM_LDS char* pb = vst + row_b * D * 2 + (((col >> 3) ^ swz_v<D>(row_b)) << 4) + (col & 7) * 2;
+        const bf16x8 a = cat(lds_read_tr(pa), lds_read_tr(pb));
+        oacc[mb] = mfma32(a, pf[c], oacc[mb]);
+      }
+    }
+  };
+
+  // --- scan the key blocks, compact the visited ones, process in chunks
+  int cnt = 0;
+  for (int base = 0; base < p.nkb; base += 256) {
+    const int kb = base + tid;
+    unsigned entry = 0;
+    bool valid = false;
+    if (kb < p.nkb) {
+      const BlockBounds bb = load_bounds(table + (long long)kb * 8);
+      const int c0 = kb * C::BC, c1 = min(N, c0 + C::BC);
+      const int wgc = tile_class(bb, r0, r1, c0, c1, p.causal != 0);
+      cnt0 += wgc == 0;
+      cnt1 += wgc == 1;
+      cnt2 += wgc == 2;
+      if (wgc != 0) {
+        valid = true;
+        const bool ragged = c1 - c0 < C::BC;
+        int bits = 0;
+#pragma unroll
+        for (int ww = 0; ww < C::NW; ++ww) {
+          const int a0 = r0 + 32 * ww;
+          int cls = 0;
+          if (a0 < N) {
+            cls = tile_class(bb, a0, min(N, a0 + 32), c0, c1, p.causal != 0);
+            if (ragged && cls == 2) cls = 1;
+          }
+          bits |= cls << (2 * ww);
+        }
+        entry = (unsigned)kb | ((unsigned)bits << 24);
+      }
+    }
+    const unsigned long long bal = __ballot(valid);
+    const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+    if (lane == 0) wsum[w] = __builtin_popcountll(bal);
+    __syncthreads();
+    int off = cnt, add = 0;
+#pragma unroll
+    for (int ww = 0; ww < C::NW; ++ww) {
+      const int v = wsum[ww];
+      if (ww < w) off += v;
+      add += v;
+    }
+    if (valid) list[off + rank] = (int)entry;
+    __syncthreads();
+    cnt += add;
+    if (cnt > C::LIST - 256 || base + 256 >= p.nkb) {
+      // process the compacted list with a two-stage load pipeline
+      auto step = [&](int it, auto stage_c) {
+        constexpr int S = decltype(stage_c)::value;
+        const unsigned entry_it = (unsigned)list[it];
+        if (it + 1 < cnt) {
+          issue((unsigned)list[it + 1], std::integral_constant<int, 1 - S>{});
+          wait_vmcnt<C::LOADS_PER_TILE>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        lds_barrier();
+        compute(entry_it, stage_c);
+        lds_barrier();
+      };
+      if (cnt > 0) issue((unsigned)list[0], std::integral_constant<int, 0>{});
+      for (int it = 0; it < cnt; it += 2) {
+        step(it, std::integral_constant<int, 0>{});
+        if (it + 1 < cnt) step(it + 1, std::integral_constant<int, 1>{});
+      }
+      cnt = 0;
+    }
+  }
+
+  // --- epilogue: normalise, store O (bf16) and the natural-log LSE
+  const float lt = l_run + xor32(l_run);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (i < N) {
+    bf16* og = reinterpret_cast<bf16*>(p.o) + (slice + i) * D;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[mb][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(og + 32 * mb + 8 * g + 4 * hh) = v4;
+      }
+    if (hh == 0) p.lse[slice + i] = lt > 0.f ? m_run * p.scale + __logf(lt) : kNegInf;
+  }
+  if (p.counts != nullptr) {
+    atomicAdd(&wcount[0], cnt0);
+    atomicAdd(&wcount[1], cnt1);
+    atomicAdd(&wcount[2], cnt2);
+    __syncthreads();
+    if (tid < 3) atomicAdd(p.counts + tid, (unsigned long long)wcount[tid]);
+  }
+}
+
+// ---------------------------------------------------------------- fp32 kernel
+// Same tiling and classification with v_mfma_f32_32x32x2_f32; K and V tiles
+// are staged through registers into padded LDS rows. Probabilities stay fp32.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
+  constexpr int BC = 64, BR = 128, KS = D + 1, VS = D + 4;
+  __shared__ float ks[BC * KS];
+  __shared__ float vs[BC * VS];
+  __shared__ int vl[4 * 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int hh = lane >> 5;
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;
+  const int qb = p.nqb - 1 - (int)(blockIdx.x / BH);
+  const int b = bh / p.H, h = bh % p.H;
+  const int hmi = p.hm == 1 ? 0 : h;
+  const int N = p.N;
+  const long long slice = (long long)bh * N;
+  const int r0 = qb * BR, r1 = min(N, r0 + BR);
+  const int i = r0 + 32 * w + (lane & 31);
+  const float* qg = reinterpret_cast<const float*>(p.q) + slice * D;
+  const float* kg = reinterpret_cast<const float*>(p.k) + slice * D;
+  const float* vg = reinterpret_cast<const float*>(p.v) + slice * D;
+  const long long vrow = ((long long)b * p.hm + hmi) * N;
+  const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb * 8;
+
+  float qf[D / 2];
+#pragma unroll
+  for (int t = 0; t < D / 2; ++t) qf[t] = i < N ? qg[(long long)i * D + 2 * t + hh] : 0.f;
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+  unsigned cnt0 = 0, cnt1 = 0, cnt2 = 0;
+
+  for (int kb = 0; kb < p.nkb; ++kb) {
+    const BlockBounds bb = load_bounds(table + (long long)kb * 8);
+    const int c0 = kb * BC, c1 = min(N, c0 + BC);
+    const int wgc = tile_class(bb, r0, r1, c0, c1, p.causal != 0);
+    cnt0 += wgc == 0;
+    cnt1 += wgc == 1;
+    cnt2 += wgc == 2;
+    if (wgc == 0) continue;
+    int wc = 0;
+    const int a0 = r0 + 32 * w;
+    if (a0 < N) {
+      wc = tile_class(bb, a0, min(N, a0 + 32), c0, c1, p.causal != 0);
+      if (c1 - c0 < BC && wc == 2) wc = 1;
+    }
+    __syncthreads();
+    for (int t = tid; t < BC * D; t += 256) {
+      const int row = t / D, col = t % D;
+      const bool ok = c0 + row < N;
+      ks[row * KS + col] = ok ? kg[(long long)(c0 + row) * D + col] : 0.f;
+      vs[row * VS + col] = ok ? vg[(long long)(c0 + row) * D + col] : 0.f;
+    }
+    {
+      const int vsel = tid >> 6, kk = tid & 63;
+      const int32_t* src = vsel == 0 ? p.lts : vsel == 1 ? p.lte : vsel == 2 ? p.uts : p.ute;
+      const bool present = src != nullptr && (vsel < 2 ? p.has_lt : p.has_ut);
+      vl[vsel * 64 + kk] = (present && c0 + kk < N) ? src[vrow + c0 + kk] : 0;
+    }
+    __syncthreads();
+    if (wc == 0) continue;
+    f32x16 s[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      s[jb] = f32x16{};
+      const int row = jb * 32 + (lane & 31);
+#pragma unroll
+      for (int t = 0; t < D / 2; ++t) s[jb] = mfma32f(ks[row * KS + 2 * t + hh], qf[t], s[jb]);
+    }
+    if (wc == 1) {
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) mask_block(s[jb], (const FM_LDS int*)vl, jb * 32, c0, i, p, hh);
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = exp2f((m_run - m_use) * p.sl2);
+    const float msl = m_use * p.sl2;
+    float rs = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[jb][r] = exp2f(__builtin_fmaf(s[jb][r], p.sl2, -msl));
+        rs += s[jb][r];
+      }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int key = jb * 32 + 8 * (t / 4) + 4 * hh + (t % 4);
+          oacc[mb] = mfma32f(vs[key * VS + 32 * mb + (lane & 31)], s[jb][t], oacc[mb]);
+        }
+  }
+
+  const float lt = l_run + xor32(l_run);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (i < N) {
+    float* og = reinterpret_cast<float*>(p.o) + (slice + i) * D;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = oacc[mb][4 * g + e] * inv;
+        *reinterpret_cast<f32x4*>(og + 32 * mb + 8 * g + 4 * hh) = v4;
+      }
+    if (hh == 0) p.lse[slice + i] = lt > 0.f ? m_run * p.scale + logf(lt) : kNegInf;
+  }
+  if (p.counts != nullptr && tid == 0) {
+    atomicAdd(p.counts + 0, (unsigned long long)cnt0);
+    atomicAdd(p.counts + 1, (unsigned long long)cnt1);
+    atomicAdd(p.counts + 2, (unsigned long long)cnt2);
+  }
+}
+
+// ---------------------------------------------------------------- launch
+template <int D>
+static hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
+  const long long grid = (long long)p.B * p.H * p.nqb;
+  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream) {
+  const long long grid = (long long)p.B * p.H * p.nqb;
+  hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
+  FwdParams p{};
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.lts = a.mask.lts;
+  p.lte = a.mask.lte;
+  p.uts = a.mask.uts;
+  p.ute = a.mask.ute;
+  p.table = a.table;
+  p.o = a.out;
+  p.lse = a.lse_out;
+  p.counts = a.tile_counts;
+  p.B = a.B;
+  p.H = a.H;
+  p.N = a.N;
+  p.hm = a.mask.hm;
+  p.causal = a.mask.causal;
+  p.has_lt = a.mask.lts != nullptr;
+  p.has_lte = a.mask.lts != nullptr && a.mask.lte != nullptr;
+  p.has_ut = !a.mask.causal && a.mask.uts != nullptr && a.mask.ute != nullptr;
+  p.scale = a.scale;
+  p.sl2 = a.scale * kLog2e;
+  p.nqb = (a.N + kFwdBlockQ - 1) / kFwdBlockQ;
+  p.nkb = (a.N + kFwdBlockK - 1) / kFwdBlockK;
+  if (a.is_bf16) {
+    switch (a.d) {
+      case 64: return launch_fwd_bf16<64>(p, stream);
+      case 128: return launch_fwd_bf16<128>(p, stream);
+      case 256: return launch_fwd_bf16<256>(p, stream);
+    }
+  } else {
+    switch (a.d) {
+      case 64: return launch_fwd_f32<64>(p, stream);
+      case 128: return launch_fwd_f32<128>(p, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fm

@@ -1,0 +1,57 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fm {
+
+// Column granularity of the key-block table the attention kernels consume.
+constexpr int kTableBlock = 64;
+
+// Tile shapes the attention kernels classify (query rows x key columns).
+constexpr int kFwdBlockQ = 128;
+constexpr int kFwdBlockK = 64;
+constexpr int kBwdBlockQ = 64;
+constexpr int kBwdBlockK = 128;
+
+struct MaskArgs {
+  const int32_t* lts;  // [B, hm, N] or nullptr
+  const int32_t* lte;
+  const int32_t* uts;
+  const int32_t* ute;
+  int hm;
+  int causal;
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;      // backward input (forward output)
+  const float* lse;   // backward input
+  const void* dout;   // backward input
+  MaskArgs mask;
+  const int32_t* table;  // [B, hm, ceil(N / kTableBlock), 8]
+  int B, H, N, d, dv;
+  int is_bf16;
+  float scale;
+  void* out;          // forward: O
+  float* lse_out;     // forward: logsumexp
+  void* dq;
+  void* dk;
+  void* dv_out;
+  float* dq_acc;      // backward workspace: float32 [B, H, N, d]
+  float* delta;       // backward workspace: float32 [B, H, N]
+  unsigned long long* tile_counts;
+};
+
+hipError_t launch_kblock_minmax(const MaskArgs& m, int B, int N, int block, int32_t* out,
+                                hipStream_t stream);
+hipError_t launch_classify(const int32_t* table, int B, int hm, int N, int causal, int block_q,
+                           int block_k, int8_t* out, hipStream_t stream);
+hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace fm

@@ -1,0 +1,124 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching the GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_masked_attention_amd import _binding
+from _lib_fixture import ensure_built
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashmask.h")
+
+FM_SUCCESS, FM_INVALID, FM_NOT_SUPPORTED, FM_WS_SMALL, FM_HIP = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ensure_built()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(flashmask_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = declared_symbols()
+    for n in ["flashmask_tile_classify", "flashmask_fwd", "flashmask_bwd",
+              "flashmask_workspace_size", "flashmask_status_string", "flashmask_table_block",
+              "flashmask_tile_shape"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (flashmask_\w+)", out))
+    for n in declared_symbols():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert _binding.status_string(s)
+    assert _binding.status_string(99) == "unknown status"
+
+
+def test_table_block_and_tile_shapes(lib):
+    import torch
+    assert _binding.table_block() == 64
+    assert _binding.tile_shape(False, 128, torch.bfloat16) == (128, 64)
+    assert _binding.tile_shape(True, 128, torch.bfloat16) == (64, 128)
+    with pytest.raises(_binding.FlashMaskError):
+        _binding.tile_shape(False, 96, torch.bfloat16)
+
+
+def test_workspace_size(lib):
+    import torch
+    fwd = _binding.workspace_size(False, 1, 32, 8192, 128, 128, 1, torch.bfloat16)
+    assert fwd == 128 * 8 * 4              # the table: 128 key blocks x 8 int32
+    bwd = _binding.workspace_size(True, 1, 32, 8192, 128, 128, 1, torch.bfloat16)
+    assert bwd == 4096 + 32 * 8192 * 4 + 32 * 8192 * 128 * 4
+    assert _binding.workspace_size(False, 1, 1, 10, 96, 96, 1, torch.bfloat16) == 0
+
+
+def _fwd_call(lib, q=1, k=1, v=1, o=1, lse=1, hm=1, B=1, H=2, N=16, d=128, dv=128,
+              dtype=1, causal=1, table=None, ws=None, ws_bytes=0, uts=None, ute=None):
+    p = lambda x: None if x is None else ctypes.c_void_p(x * 256)
+    return lib.flashmask_fwd(p(q), p(k), p(v), p(1), None, p(uts), p(ute), hm, p(table),
+                             B, H, N, d, dv, dtype, causal, 0.0, p(o), p(lse), None,
+                             p(ws), ws_bytes, None)
+
+
+def test_fwd_argument_checks(lib):
+    assert _fwd_call(lib, q=None) == FM_INVALID
+    assert _fwd_call(lib, o=None) == FM_INVALID
+    assert _fwd_call(lib, hm=3, H=4) == FM_INVALID
+    assert _fwd_call(lib, B=-1) == FM_INVALID
+    assert _fwd_call(lib, d=96, dv=96) == FM_NOT_SUPPORTED
+    assert _fwd_call(lib, d=128, dv=64) == FM_NOT_SUPPORTED
+    assert _fwd_call(lib, dtype=0, d=256, dv=256) == FM_NOT_SUPPORTED
+    assert _fwd_call(lib, dtype=7) == FM_INVALID
+    assert _fwd_call(lib, ws=None) == FM_WS_SMALL
+    assert _fwd_call(lib, ws=1, ws_bytes=8) == FM_WS_SMALL
+    # non-causal with only one of the upper vectors
+    assert _fwd_call(lib, causal=0, uts=1, ute=None) == FM_INVALID
+    # empty problems succeed without touching anything
+    assert _fwd_call(lib, q=None, N=0) == FM_SUCCESS
+    assert _fwd_call(lib, q=None, B=0) == FM_SUCCESS
+
+
+def test_bwd_argument_checks(lib):
+    p = lambda x: None if x is None else ctypes.c_void_p(x * 256)
+
+    def call(dq=1, ws=1, ws_bytes=1 << 40, d=128, N=16):
+        return lib.flashmask_bwd(p(1), p(1), p(1), p(1), p(1), p(1), p(1), None, None, None, 1, None,
+                                 1, 2, N, d, d, 1, 1, 0.0, p(dq), p(1), p(1), None, p(ws),
+                                 ws_bytes, None)
+    assert call(dq=None) == FM_INVALID
+    assert call(ws=None) == FM_WS_SMALL
+    assert call(ws_bytes=16) == FM_WS_SMALL
+    assert call(d=80) == FM_NOT_SUPPORTED
+    assert call(dq=None, N=0) == FM_SUCCESS
+
+
+def test_classify_argument_checks(lib):
+    p = lambda x: None if x is None else ctypes.c_void_p(x * 256)
+    assert lib.flashmask_tile_classify(p(1), p(1), None, None, 1, 1, 16, 1, 0, 64, p(1), None, None) == FM_INVALID
+    assert lib.flashmask_tile_classify(p(1), p(1), None, None, 1, 1, 16, 1, 64, 64, None, None, None) == FM_INVALID
+    assert lib.flashmask_tile_classify(p(1), p(1), None, None, 1, 0, 16, 1, 64, 64, p(1), None, None) == FM_INVALID
+    assert lib.flashmask_tile_classify(p(1), p(1), p(1), None, 1, 1, 16, 0, 64, 64, p(1), None, None) == FM_INVALID
+    assert lib.flashmask_tile_classify(None, None, None, None, 1, 1, 0, 1, 64, 64, None, None, None) == FM_SUCCESS
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    m = _binding.Mask(None, None, None, None, True)
+    with pytest.raises(ValueError):
+        _binding.fwd(q, q, q, m)

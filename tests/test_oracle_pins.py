@@ -359,12 +359,13 @@ def test_table_is_blockwise_min_max(seed):
         np.testing.assert_array_equal(tab[0, 0, :, 2 * t + 1], np.maximum.reduceat(x, cut))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 @pytest.mark.parametrize("causal", [True, False])
 def test_classes_sound_on_arbitrary_vectors(seed, causal):
     rng = np.random.default_rng(seed)
     n = int(rng.integers(1, 200))
-    bq, bk = int(rng.choice([4, 8, 16, 32])), int(rng.choice([4, 8, 16, 32]))
+    sizes = [1, 2, 3, 4, 5, 7, 8, 16, 32]
+    bq, bk = int(rng.choice(sizes)), int(rng.choice(sizes))
     # intervals built from random centres so that some tiles are hidden whole
     c = rng.integers(-20, n + 20, n)
     w = rng.integers(0, n + 40, n)
@@ -392,6 +393,17 @@ def test_classes_exact_on_block_aligned(family):
     tab = oracle.kblock_minmax(1, 1, n, blk, m.lts[None, None], m.lte[None, None])
     cls = oracle.classify(tab, n, blk, blk, True)[0, 0]
     np.testing.assert_array_equal(cls, _brute_classes(masked, n, blk, blk))
+
+
+@pytest.mark.parametrize("bq,bk", [(3, 5), (5, 3), (7, 2), (4, 6)])
+def test_classes_exact_on_causal_with_unaligned_blocks(bq, bk):
+    # the causal edge cuts tiles at every offset; empty intervals leave only it
+    n = 97
+    m = I.causal_only(n)
+    masked = oracle.dense_mask(n, True, **_rows(m))
+    tab = oracle.kblock_minmax(1, 1, n, bk, m.lts[None, None], m.lte[None, None])
+    cls = oracle.classify(tab, n, bq, bk, True)[0, 0]
+    np.testing.assert_array_equal(cls, _brute_classes(masked, n, bq, bk))
 
 
 def test_table_neutral_values_for_missing_vectors():
