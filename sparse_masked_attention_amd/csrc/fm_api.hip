@@ -23,10 +23,8 @@ bool supported(int d, int dv, fm_dtype_t dtype) {
   return false;
 }
 
-// Backward kernels compiled so far: bf16 with d = dv in {64, 128}.
-bool bwd_supported(int d, int dv, fm_dtype_t dtype) {
-  return d == dv && dtype == FM_BF16 && (d == 64 || d == 128);
-}
+// Backward kernels: bf16 with d = dv in {64, 128, 256}, fp32 with {64, 128}.
+bool bwd_supported(int d, int dv, fm_dtype_t dtype) { return supported(d, dv, dtype); }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -89,7 +87,7 @@ int flashmask_table_block(void) { return kTableBlock; }
 fm_status_t flashmask_tile_shape(int is_bwd, int d, fm_dtype_t dtype, int* block_q, int* block_k) {
   if (block_q == nullptr || block_k == nullptr) return FM_ERROR_INVALID_VALUE;
   if (!supported(d, d, dtype)) return FM_ERROR_NOT_SUPPORTED;
-  *block_q = is_bwd ? fm::kBwdBlockQ : fm::kFwdBlockQ;
+  *block_q = is_bwd ? fm::bwd_block_q(d, dtype == FM_BF16) : fm::kFwdBlockQ;
   *block_k = is_bwd ? fm::kBwdBlockK : fm::kFwdBlockK;
   return FM_SUCCESS;
 }

@@ -110,17 +110,22 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------- main kernel
+// d = 256 does not fit dK and dV of 32 keys per wave in registers; it runs as
+// two workgroups per key block, each owning half of the output columns (of
+// dK, dV and dQ) and recomputing S and dP in full.
 template <int D>
 struct BwdCfg {
   static constexpr int NW = 4;
   static constexpr int KW = 32;                 // keys per wave
   static constexpr int BKC = NW * KW;           // keys per workgroup
-  static constexpr int BQ = 64;                 // query rows per step
+  static constexpr int NSPLIT = D > 128 ? 2 : 1;
+  static constexpr int DO = D / NSPLIT;         // output columns per workgroup
+  static constexpr int BQ = D > 128 ? 32 : 64;  // query rows per step
   static constexpr int CH = D / 8;
   static constexpr int QT = BQ * D * 2;         // bytes of one Q or dO tile
   static constexpr int LOADS = QT / (NW * 1024);
   static constexpr int STAGE = 2 * QT + 2 * BQ * 4;  // Q, dO, LSE, delta
-  static constexpr int KT = BKC * D * 2;        // resident K tile (dQ operand)
+  static constexpr int KT = BKC * DO * 2;       // resident K columns (dQ operand)
   static constexpr int KLOADS = KT / (NW * 1024);
   static constexpr int DSS = BQ + 8;            // dS^T row stride (bf16), padded
   static constexpr int DS = BKC * DSS * 2;
@@ -130,16 +135,16 @@ struct BwdCfg {
 
 // Chunk swizzle shared by row reads (32 rows, one chunk) and transposed reads
 // (8 rows x 4 chunks) of the Q, dO and K tiles.
-template <int D>
+template <int W>
 __device__ inline int swz(int row) {
-  if constexpr (D >= 128) return 4 * (row & 3) + ((row >> 2) & 3);
+  if constexpr (W >= 128) return 4 * (row & 3) + ((row >> 2) & 3);
   else return 4 * (row & 1) + ((row >> 1) & 3);
 }
 
-template <int D>
+// byte address of element (row, col) of a swizzled row-major bf16 tile W wide
+template <int W>
 __device__ inline const FM_LDS char* tile_addr(const FM_LDS char* base, int row, int col) {
-  // byte address of element (row, col) of a swizzled row-major bf16 tile
-  return base + row * D * 2 + (((col >> 3) ^ swz<D>(row)) << 4) + (col & 7) * 2;
+  return base + row * W * 2 + (((col >> 3) ^ swz<W>(row)) << 4) + (col & 7) * 2;
 }
 
 template <int D>
@@ -160,7 +165,10 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
   const int l32 = lane & 31;
   const int BH = p.B * p.H;
   const int bh = blockIdx.x % BH;
-  const int kb = (int)(blockIdx.x / BH);     // heavy (early) key blocks first
+  const int rest = (int)(blockIdx.x / BH);   // heavy (early) key blocks first
+  const int kb = rest / C::NSPLIT;
+  const int sp = rest % C::NSPLIT;           // which output column half
+  const int col0 = sp * C::DO;
   const int b = bh / p.H, h = bh % p.H;
   const int hmi = p.hm == 1 ? 0 : h;
   const int N = p.N;
@@ -178,13 +186,14 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t rlse = make_rsrc(p.lse + slice, (uint32_t)N * 4);
   const __amdgpu_buffer_rsrc_t rdel = make_rsrc(p.delta + slice, (uint32_t)N * 4);
 
-  // K tile of the workgroup's keys into LDS (dQ operand), rows past N zero
+  // K columns [col0, col0 + DO) of the workgroup's keys into LDS (dQ
+  // operand); rows past N read as zero
 #pragma unroll
   for (int u = 0; u < C::KLOADS; ++u) {
     const int g = (w * C::KLOADS + u) * 64 + lane;
-    const int row = g / C::CH, pch = g % C::CH;
+    const int row = g / (C::DO / 8), pch = g % (C::DO / 8);
     load_lds16(rk, (FM_LDS char*)ktile + (w * C::KLOADS + u) * 1024,
-               (uint32_t)((c0 + row) * D + 8 * (pch ^ swz<D>(row))) * 2);
+               (uint32_t)((c0 + row) * D + col0 + 8 * (pch ^ swz<C::DO>(row))) * 2);
   }
   // K and V of this lane's key as the B operands of S = Q K^T and dP = dO V^T
   bf16x8 kB[D / 16], vB[D / 16];
@@ -207,9 +216,9 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
     }
   }
 
-  f32x16 dvacc[D / 32], dkacc[D / 32];
+  f32x16 dvacc[C::DO / 32], dkacc[C::DO / 32];
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) {
+  for (int mb = 0; mb < C::DO / 32; ++mb) {
     dvacc[mb] = f32x16{};
     dkacc[mb] = f32x16{};
   }
@@ -314,8 +323,8 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
         const int ra = 16 * c + 4 * hh + (sl >> 2);
         const int rb = ra + 8;
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) {
-          const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+        for (int mb = 0; mb < C::DO / 32; ++mb) {
+          const int col = col0 + 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
           const bf16x8 bo = cat(lds_read_tr(tile_addr<D>(dost, ra, col)), lds_read_tr(tile_addr<D>(dost, rb, col)));
           dvacc[mb] = mfma32(pB[c], bo, dvacc[mb]);
           const bf16x8 bq = cat(lds_read_tr(tile_addr<D>(qst, ra, col)), lds_read_tr(tile_addr<D>(qst, rb, col)));
@@ -327,9 +336,9 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
     // dQ over all 128 keys: the step's (BQ/32) x (D/32) output blocks of 32x32
     // are split evenly over the waves; a wave's blocks share one row block.
     {
-      constexpr int BPW = (C::BQ / 32) * (D / 32) / C::NW;
+      constexpr int BPW = (C::BQ / 32) * (C::DO / 32) / C::NW;
       const int ob0 = w * BPW;
-      const int ib = ob0 / (D / 32);
+      const int ib = ob0 / (C::DO / 32);
       const int sl = lane & 15;
       f32x16 dq[BPW];
 #pragma unroll
@@ -343,21 +352,21 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
         const bf16x8 a = cat(lds_read_tr(d0), lds_read_tr(d0 + 4 * C::DSS));
 #pragma unroll
         for (int t = 0; t < BPW; ++t) {
-          const int mb = (ob0 + t) % (D / 32);
+          const int mb = (ob0 + t) % (C::DO / 32);
           const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
-          const bf16x8 bk = cat(lds_read_tr(tile_addr<D>((const FM_LDS char*)ktile, kr, col)),
-                                lds_read_tr(tile_addr<D>((const FM_LDS char*)ktile, kr + 4, col)));
+          const bf16x8 bk = cat(lds_read_tr(tile_addr<C::DO>((const FM_LDS char*)ktile, kr, col)),
+                                lds_read_tr(tile_addr<C::DO>((const FM_LDS char*)ktile, kr + 4, col)));
           dq[t] = mfma32(a, bk, dq[t]);
         }
       }
       // add into the float32 accumulator (lane holds column 32mb + lane % 32)
 #pragma unroll
       for (int t = 0; t < BPW; ++t) {
-        const int mb = (ob0 + t) % (D / 32);
+        const int mb = (ob0 + t) % (C::DO / 32);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int i = q0 + 32 * ib + 8 * (r / 4) + 4 * hh + (r % 4);
-          if (i < N) unsafeAtomicAdd(p.dq_acc + (slice + i) * D + 32 * mb + l32, dq[t][r]);
+          if (i < N) unsafeAtomicAdd(p.dq_acc + (slice + i) * D + col0 + 32 * mb + l32, dq[t][r]);
         }
       }
     }
@@ -452,22 +461,191 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
     bf16* dkg = reinterpret_cast<bf16*>(p.dk) + slice * D;
     bf16* dvg = reinterpret_cast<bf16*>(p.dv) + slice * D;
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb)
+    for (int mb = 0; mb < C::DO / 32; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = wc0 + 8 * (r / 4) + 4 * hh + (r % 4);
         if (key < N) {
-          dkg[(long long)key * D + 32 * mb + l32] = (bf16)dkacc[mb][r];
-          dvg[(long long)key * D + 32 * mb + l32] = (bf16)dvacc[mb][r];
+          dkg[(long long)key * D + col0 + 32 * mb + l32] = (bf16)dkacc[mb][r];
+          dvg[(long long)key * D + col0 + 32 * mb + l32] = (bf16)dvacc[mb][r];
         }
       }
   }
-  if (p.counts != nullptr) {
+  if (p.counts != nullptr && sp == 0) {
     atomicAdd(&wcount[0], cnt0);
     atomicAdd(&wcount[1], cnt1);
     atomicAdd(&wcount[2], cnt2);
     __syncthreads();
     if (tid < 3) atomicAdd(p.counts + tid, (unsigned long long)wcount[tid]);
+  }
+}
+
+// ---------------------------------------------------------------- fp32 kernel
+// Same decomposition with v_mfma_f32_32x32x2_f32 and everything staged
+// through LDS with plain loads (no pipelining): 4 waves x 32 keys, query
+// steps of 32 rows. K and V of the lane's key sit in registers as B operands.
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_f32_kernel(BwdParams p) {
+  constexpr int NW = 4, KW = 32, BKC = 128, BQ = 32, S1 = D + 1, DSS = BKC + 1;
+  __shared__ float qs[BQ * S1];
+  __shared__ float dos[BQ * S1];
+  __shared__ float ks[BKC * S1];
+  __shared__ float dss[BQ * DSS];
+  __shared__ float lse_s[BQ];
+  __shared__ float del_s[BQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;
+  const int kb = (int)(blockIdx.x / BH);
+  const int b = bh / p.H, h = bh % p.H;
+  const int hmi = p.hm == 1 ? 0 : h;
+  const int N = p.N;
+  const long long slice = (long long)bh * N;
+  const int c0 = kb * BKC, c1 = min(N, c0 + BKC);
+  const int wc0 = c0 + KW * w;
+  const int j = wc0 + l32;
+  const float* qg = reinterpret_cast<const float*>(p.q) + slice * D;
+  const float* kg = reinterpret_cast<const float*>(p.k) + slice * D;
+  const float* vg = reinterpret_cast<const float*>(p.v) + slice * D;
+  const float* dog = reinterpret_cast<const float*>(p.dout) + slice * D;
+
+  for (int t = tid; t < BKC * D; t += 256) {
+    const int row = t / D, col = t % D;
+    ks[row * S1 + col] = c0 + row < N ? kg[(long long)(c0 + row) * D + col] : 0.f;
+  }
+  float kr[D / 2], vr[D / 2];
+#pragma unroll
+  for (int t = 0; t < D / 2; ++t) {
+    kr[t] = j < N ? kg[(long long)j * D + 2 * t + hh] : 0.f;
+    vr[t] = j < N ? vg[(long long)j * D + 2 * t + hh] : 0.f;
+  }
+  const long long vrow = ((long long)b * p.hm + hmi) * N;
+  int k_lts = N, k_lte = N, k_uts = 0, k_ute = 0;
+  if (j < N) {
+    if (p.has_lt) {
+      k_lts = p.lts[vrow + j];
+      k_lte = p.has_lte ? p.lte[vrow + j] : N;
+    }
+    if (p.has_ut) {
+      k_uts = p.uts[vrow + j];
+      k_ute = p.ute[vrow + j];
+    }
+  }
+  f32x16 dvacc[D / 32], dkacc[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+    dvacc[mb] = f32x16{};
+    dkacc[mb] = f32x16{};
+  }
+  const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb64 * 8;
+  BlockBounds kbnd = load_bounds(table + (long long)(c0 / 64) * 8);
+  if (c0 / 64 + 1 < p.nkb64) {
+    const BlockBounds q = load_bounds(table + (long long)(c0 / 64 + 1) * 8);
+    kbnd.lts_mn = min(kbnd.lts_mn, q.lts_mn); kbnd.lts_mx = max(kbnd.lts_mx, q.lts_mx);
+    kbnd.lte_mn = min(kbnd.lte_mn, q.lte_mn); kbnd.lte_mx = max(kbnd.lte_mx, q.lte_mx);
+    kbnd.uts_mn = min(kbnd.uts_mn, q.uts_mn); kbnd.uts_mx = max(kbnd.uts_mx, q.uts_mx);
+    kbnd.ute_mn = min(kbnd.ute_mn, q.ute_mn); kbnd.ute_mx = max(kbnd.ute_mx, q.ute_mx);
+  }
+  const BlockBounds wbnd = load_bounds(table + (long long)(min(wc0, N - 1) / 64) * 8);
+  unsigned cnt0 = 0, cnt1 = 0, cnt2 = 0;
+
+  for (int qb = 0; qb < p.nqb; ++qb) {
+    const int q0 = qb * BQ, q1 = min(N, q0 + BQ);
+    const int wgc = tile_class(kbnd, q0, q1, c0, c1, p.causal != 0);
+    cnt0 += wgc == 0;
+    cnt1 += wgc == 1;
+    cnt2 += wgc == 2;
+    if (wgc == 0) continue;
+    int wc = 0;
+    if (wc0 < N) {
+      wc = tile_class(wbnd, q0, q1, wc0, min(N, wc0 + KW), p.causal != 0);
+      if (wc == 2 && (q1 - q0 < BQ || c1 - c0 < BKC)) wc = 1;
+    }
+    __syncthreads();  // previous step's readers are done
+    for (int t = tid; t < BQ * D; t += 256) {
+      const int row = t / D, col = t % D;
+      const bool ok = q0 + row < N;
+      qs[row * S1 + col] = ok ? qg[(long long)(q0 + row) * D + col] : 0.f;
+      dos[row * S1 + col] = ok ? dog[(long long)(q0 + row) * D + col] : 0.f;
+    }
+    if (tid < BQ) {
+      const bool ok = q0 + tid < N;
+      const float l = ok ? p.lse[slice + q0 + tid] : 0.f;
+      lse_s[tid] = l == kNegInf ? __builtin_inff() : l * kLog2e;
+      del_s[tid] = ok ? p.delta[slice + q0 + tid] : 0.f;
+    }
+    __syncthreads();
+    f32x16 pr = f32x16{}, dsr = f32x16{};
+    if (wc != 0) {
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int t = 0; t < D / 2; ++t) {
+        sacc = mfma32f(qs[l32 * S1 + 2 * t + hh], kr[t], sacc);
+        dpacc = mfma32f(dos[l32 * S1 + 2 * t + hh], vr[t], dpacc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int il = 8 * (r / 4) + 4 * hh + (r % 4);
+        const int i = q0 + il;
+        float sv = sacc[r];
+        if (wc == 1) {
+          bool m = (i >= N) || (j >= N) || (p.causal && j > i);
+          m = m || (k_lts <= i && i < k_lte) || (k_uts <= i && i < k_ute);
+          if (m) sv = kNegInf;
+        }
+        const float pv = exp2f(__builtin_fmaf(sv, p.sl2, -lse_s[il]));
+        pr[r] = pv;
+        dsr[r] = pv * (dpacc[r] - del_s[il]) * p.scale;
+      }
+      // dV += P^T dO and dK += dS^T Q over the step's 32 rows
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int il = 8 * (t / 4) + 4 * hh + (t % 4);
+          dvacc[mb] = mfma32f(pr[t], dos[il * S1 + 32 * mb + l32], dvacc[mb]);
+          dkacc[mb] = mfma32f(dsr[t], qs[il * S1 + 32 * mb + l32], dkacc[mb]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dss[(8 * (r / 4) + 4 * hh + (r % 4)) * DSS + KW * w + l32] = dsr[r];
+    __syncthreads();
+    // dQ over the 128 keys; output blocks of 32 columns spread over the waves
+    for (int mb = w; mb < D / 32; mb += NW) {
+      f32x16 dq = f32x16{};
+#pragma unroll 8
+      for (int t = 0; t < BKC / 2; ++t)
+        dq = mfma32f(dss[l32 * DSS + 2 * t + hh], ks[(2 * t + hh) * S1 + 32 * mb + l32], dq);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = q0 + 8 * (r / 4) + 4 * hh + (r % 4);
+        if (i < N) unsafeAtomicAdd(p.dq_acc + (slice + i) * D + 32 * mb + l32, dq[r]);
+      }
+    }
+  }
+  if (wc0 < N) {
+    float* dkg = reinterpret_cast<float*>(p.dk) + slice * D;
+    float* dvg = reinterpret_cast<float*>(p.dv) + slice * D;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = wc0 + 8 * (r / 4) + 4 * hh + (r % 4);
+        if (key < N) {
+          dkg[(long long)key * D + 32 * mb + l32] = dkacc[mb][r];
+          dvg[(long long)key * D + 32 * mb + l32] = dvacc[mb][r];
+        }
+      }
+  }
+  if (p.counts != nullptr && tid == 0) {
+    atomicAdd(p.counts + 0, (unsigned long long)cnt0);
+    atomicAdd(p.counts + 1, (unsigned long long)cnt1);
+    atomicAdd(p.counts + 2, (unsigned long long)cnt2);
   }
 }
 
@@ -491,14 +669,27 @@ static hipError_t launch_convert(const BwdParams& p, int d, hipStream_t stream) 
 }
 
 template <int D>
-static hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+static hipError_t launch_bwd_bf16(BwdParams p, hipStream_t stream) {
+  p.nqb = (p.N + BwdCfg<D>::BQ - 1) / BwdCfg<D>::BQ;
   hipError_t e = launch_pre<D, bf16>(p, stream);
   if (e != hipSuccess) return e;
-  const long long grid = (long long)p.B * p.H * p.nkb;
+  const long long grid = (long long)p.B * p.H * p.nkb * BwdCfg<D>::NSPLIT;
   hipLaunchKernelGGL(bwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_convert<bf16>(p, D, stream);
+}
+
+template <int D>
+static hipError_t launch_bwd_f32(BwdParams p, hipStream_t stream) {
+  p.nqb = (p.N + 31) / 32;
+  hipError_t e = launch_pre<D, float>(p, stream);
+  if (e != hipSuccess) return e;
+  const long long grid = (long long)p.B * p.H * p.nkb;
+  hipLaunchKernelGGL(bwd_f32_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_convert<float>(p, D, stream);
 }
 
 hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
@@ -530,13 +721,18 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.has_ut = !a.mask.causal && a.mask.uts != nullptr && a.mask.ute != nullptr;
   p.scale = a.scale;
   p.sl2 = a.scale * kLog2e;
-  p.nqb = (a.N + kBwdBlockQ - 1) / kBwdBlockQ;
   p.nkb = (a.N + kBwdBlockK - 1) / kBwdBlockK;
   p.nkb64 = (a.N + kTableBlock - 1) / kTableBlock;
   if (a.is_bf16) {
     switch (a.d) {
       case 64: return launch_bwd_bf16<64>(p, stream);
       case 128: return launch_bwd_bf16<128>(p, stream);
+      case 256: return launch_bwd_bf16<256>(p, stream);
+    }
+  } else {
+    switch (a.d) {
+      case 64: return launch_bwd_f32<64>(p, stream);
+      case 128: return launch_bwd_f32<128>(p, stream);
     }
   }
   return hipErrorInvalidValue;

@@ -13,8 +13,9 @@ constexpr int kTableBlock = 64;
 // Tile shapes the attention kernels classify (query rows x key columns).
 constexpr int kFwdBlockQ = 128;
 constexpr int kFwdBlockK = 64;
-constexpr int kBwdBlockQ = 64;
 constexpr int kBwdBlockK = 128;
+// backward query-block height: 64 rows for bf16 with d <= 128, else 32
+inline int bwd_block_q(int d, int is_bf16) { return (is_bf16 && d <= 128) ? 64 : 32; }
 
 struct MaskArgs {
   const int32_t* lts;  // [B, hm, N] or nullptr

@@ -54,6 +54,8 @@ def test_table_block_and_tile_shapes(lib):
     assert _binding.table_block() == 64
     assert _binding.tile_shape(False, 128, torch.bfloat16) == (128, 64)
     assert _binding.tile_shape(True, 128, torch.bfloat16) == (64, 128)
+    assert _binding.tile_shape(True, 256, torch.bfloat16) == (32, 128)
+    assert _binding.tile_shape(True, 64, torch.float32) == (32, 128)
     with pytest.raises(_binding.FlashMaskError):
         _binding.tile_shape(False, 96, torch.bfloat16)
 

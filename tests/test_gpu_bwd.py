@@ -10,7 +10,7 @@ import torch
 import oracle
 from sparse_masked_attention_amd import inputs as I
 from sparse_masked_attention_amd import _binding as fm
-from gpu_util import check_bf16, mask_from, qkvo, say, to_dev, to_np
+from gpu_util import check_bf16, check_fp32, mask_from, qkvo, say, to_dev, to_np
 from _lib_fixture import ensure_built
 
 pytestmark = pytest.mark.gpu
@@ -30,13 +30,14 @@ def run_case(q, k, v, do, vec, dtype=torch.bfloat16, counts=None):
     return dq, dk, dv
 
 
-def compare(q, k, v, do, vec, dq, dk, dv, heads=None):
+def compare(q, k, v, do, vec, dq, dk, dv, heads=None, fp32=False):
     lts, lte, uts, ute, causal = vec
     rq, rk, rv = oracle.backward(q, k, v, do, causal, lts, lte, uts, ute, heads=heads)
     sel = (lambda x: x) if heads is None else (lambda x: np.stack([x[b, h] for b, h in heads]))
-    check_bf16("dQ", sel(to_np(dq)), sel(rq))
-    check_bf16("dK", sel(to_np(dk)), sel(rk))
-    check_bf16("dV", sel(to_np(dv)), sel(rv))
+    check = check_fp32 if fp32 else check_bf16
+    check("dQ", sel(to_np(dq)), sel(rq))
+    check("dK", sel(to_np(dk)), sel(rk))
+    check("dV", sel(to_np(dv)), sel(rv))
 
 
 FAMILIES = ["causal", "document", "share_question", "sliding_window", "block_sparse",
@@ -55,6 +56,27 @@ def test_families(family, N, d):
     compare(q, k, v, do, vec, dq, dk, dv)
 
 
+@pytest.mark.parametrize("family", ["document", "prefix_lm_document", "sliding_window", "causal"])
+def test_head_dim_256(family):
+    B, H, N, d = 1, 2, 555, 256
+    say(f"bwd family={family} N={N} d={d}")
+    q, k, v, do = qkvo(B, H, N, d, 2400, with_do=True)
+    vec = I.stack_masks([I.make_mask(family, N, np.random.default_rng(12))])
+    dq, dk, dv = run_case(q, k, v, do, vec)
+    compare(q, k, v, do, vec, dq, dk, dv)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("family", ["document", "prefix_lm_document", "all_open"])
+def test_fp32(family, d):
+    B, H, N = 1, 2, 300
+    say(f"bwd fp32 family={family} N={N} d={d}")
+    q, k, v, do = qkvo(B, H, N, d, 2500, bf16=False, with_do=True)
+    vec = I.stack_masks([I.make_mask(family, N, np.random.default_rng(13))])
+    dq, dk, dv = run_case(q, k, v, do, vec, dtype=torch.float32)
+    compare(q, k, v, do, vec, dq, dk, dv, fp32=True)
+
+
 @pytest.mark.parametrize("N", [1, 7, 64, 130])
 def test_small_and_ragged(N):
     say(f"bwd ragged N={N}")
@@ -63,6 +85,21 @@ def test_small_and_ragged(N):
         vec = I.stack_masks([I.make_mask(fam, N, np.random.default_rng(0))])
         dq, dk, dv = run_case(q, k, v, do, vec)
         compare(q, k, v, do, vec, dq, dk, dv)
+
+
+def test_tile_counts_d256_and_fp32():
+    B, H, N = 1, 2, 700
+    vec = I.stack_masks([I.make_mask("document", N, np.random.default_rng(3))])
+    lts, lte, uts, ute, causal = vec
+    for d, dtype, bf in ((256, torch.bfloat16, True), (128, torch.float32, False)):
+        say(f"bwd tile counts d={d} {dtype}")
+        q, k, v, do = qkvo(B, H, N, d, 2600, bf16=bf, with_do=True)
+        counts = torch.zeros(3, dtype=torch.int64, device="cuda")
+        run_case(q, k, v, do, vec, dtype=dtype, counts=counts)
+        bq, bk = fm.tile_shape(True, d, dtype)
+        t = oracle.kblock_minmax(B, 1, N, bk, lts, lte, uts, ute)
+        ref = oracle.classify_counts(oracle.classify(t, N, bq, bk, causal)) * H
+        assert counts.cpu().numpy().tolist() == ref.tolist()
 
 
 def test_fully_masked_rows():
@@ -91,6 +128,18 @@ def test_tile_counts_match_oracle_classes():
     t = oracle.kblock_minmax(B, 1, N, bk, lts, lte, uts, ute)
     ref = oracle.classify_counts(oracle.classify(t, N, bq, bk, causal)) * H
     assert counts.cpu().numpy().tolist() == ref.tolist()
+
+
+@pytest.mark.parametrize("family", ["causal", "document", "share_question", "sliding_window",
+                                    "block_sparse"])
+def test_full_c5_d256(family):
+    c = I.CONFIGS[5]
+    B, H, N, d = c["B"], c["H"], c["N"], 256
+    say(f"bwd full C5 family={family} d={d}")
+    q, k, v, do = (I.randn((B, H, N, d), I.qkv_seed(5, t)) for t in range(4))
+    vec = I.config_masks(5, family)
+    dq, dk, dv = run_case(q, k, v, do, vec)
+    compare(q, k, v, do, vec, dq, dk, dv, heads=[(0, 1)])
 
 
 @pytest.mark.parametrize("family", ["causal", "document", "share_question", "sliding_window",
