@@ -45,7 +45,7 @@ fm_status_t check_common(int B, int H, int N, int d, int dv, fm_dtype_t dtype, i
   if (!supported(d, dv, dtype)) return FM_ERROR_NOT_SUPPORTED;
   // 32-bit buffer offsets address one (batch, head) slice of a tensor
   if ((long long)N * d * (dtype == FM_BF16 ? 2 : 4) >= (1LL << 31)) return FM_ERROR_NOT_SUPPORTED;
-  if ((long long)B * H * ceil_div(N, fm::kFwdBlockQ) >= (1LL << 31)) return FM_ERROR_NOT_SUPPORTED;
+  if ((long long)B * H * ceil_div(N, 32) >= (1LL << 31)) return FM_ERROR_NOT_SUPPORTED;
   return FM_SUCCESS;
 }
 
@@ -87,7 +87,7 @@ int flashmask_table_block(void) { return kTableBlock; }
 fm_status_t flashmask_tile_shape(int is_bwd, int d, fm_dtype_t dtype, int* block_q, int* block_k) {
   if (block_q == nullptr || block_k == nullptr) return FM_ERROR_INVALID_VALUE;
   if (!supported(d, d, dtype)) return FM_ERROR_NOT_SUPPORTED;
-  *block_q = is_bwd ? fm::bwd_block_q(d, dtype == FM_BF16) : fm::kFwdBlockQ;
+  *block_q = is_bwd ? fm::bwd_block_q(d, dtype == FM_BF16) : fm::fwd_block_q(d, dtype == FM_BF16);
   *block_k = is_bwd ? fm::kBwdBlockK : fm::kFwdBlockK;
   return FM_SUCCESS;
 }
@@ -98,8 +98,9 @@ size_t flashmask_workspace_size(int is_bwd, int B, int H, int N, int d, int dv, 
   if (!supported(d, dv, dtype)) return 0;
   size_t bytes = align_up(table_bytes(B, hm, N));
   if (is_bwd) {
-    bytes += align_up((size_t)B * H * N * sizeof(float));                 // delta
-    bytes += align_up((size_t)B * H * N * (size_t)d * sizeof(float));     // dQ accumulator
+    bytes += 2 * align_up((size_t)B * H * N * sizeof(float));             // delta, base-2 LSE
+    if (dtype == FM_FP32)
+      bytes += align_up((size_t)B * H * N * (size_t)d * sizeof(float));   // dQ accumulator
   }
   return bytes;
 }
@@ -204,7 +205,9 @@ fm_status_t flashmask_bwd(const void* q, const void* k, const void* v, const voi
   ws += align_up(table_bytes(B, hm, N));
   a.delta = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)B * H * N * sizeof(float));
-  a.dq_acc = reinterpret_cast<float*>(ws);
+  a.lse2 = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)B * H * N * sizeof(float));
+  a.dq_acc = dtype == FM_FP32 ? reinterpret_cast<float*>(ws) : nullptr;
   a.q = q;
   a.k = k;
   a.v = v;

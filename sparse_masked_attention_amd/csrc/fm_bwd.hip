@@ -43,8 +43,9 @@ struct BwdParams {
   const int32_t* uts;
   const int32_t* ute;
   const int32_t* table;  // [B, hm, ceil(N/64), 8]
-  float* dq_acc;
+  float* dq_acc;     // fp32 path only
   float* delta;
+  float* lse2;       // logsumexp in base-2 units; +inf for fully masked rows
   void* dq;
   void* dk;
   void* dv;
@@ -56,8 +57,9 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------- preprocess
-// delta_i = sum_m dO[i][m] * O[i][m] in float32, and zero the dQ accumulator
-// rows. 16 threads per row; each handles 16-byte chunks.
+// delta_i = sum_m dO[i][m] * O[i][m] in float32; LSE in base-2 units (+inf
+// where the row is fully masked, so exp2(s - LSE2) is 0 there); for the fp32
+// path also zero the dQ accumulator rows. 16 threads per row, 16-byte chunks.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   const long long rows = (long long)p.B * p.H * p.N;
@@ -82,13 +84,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
         for (int e = 0; e < 4; ++e) acc += x[e] * y[e];
       }
     }
-    float* dqa = p.dq_acc + row * D;
+    if constexpr (sizeof(T) == 4) {
+      float* dqa = p.dq_acc + row * D;
 #pragma unroll
-    for (int c = t; c < D / 4; c += 16) *reinterpret_cast<f32x4*>(dqa + 4 * c) = f32x4{};
+      for (int c = t; c < D / 4; c += 16) *reinterpret_cast<f32x4*>(dqa + 4 * c) = f32x4{};
+    }
   }
 #pragma unroll
   for (int s = 8; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 16);
-  if (row < rows && t == 0) p.delta[row] = acc;
+  if (row < rows && t == 0) {
+    p.delta[row] = acc;
+    const float l = p.lse[row];
+    p.lse2[row] = l == kNegInf ? __builtin_inff() : l * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------- dQ convert
@@ -109,10 +117,14 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
   }
 }
 
-// ---------------------------------------------------------------- main kernel
+// ---------------------------------------------------------------- dK / dV kernel
+// Key-major: a workgroup (4 waves) owns 128 keys, 32 per wave, and walks the
+// query blocks the mask leaves visible. K and V of the lane's key are MFMA B
+// operands held in registers; dK and dV accumulate in registers. dQ is not
+// formed here (the query-major dQ pass does it without atomics).
 // d = 256 does not fit dK and dV of 32 keys per wave in registers; it runs as
-// two workgroups per key block, each owning half of the output columns (of
-// dK, dV and dQ) and recomputing S and dP in full.
+// two workgroups per key block, each owning half of the dK/dV columns and
+// recomputing S and dP in full.
 template <int D>
 struct BwdCfg {
   static constexpr int NW = 4;
@@ -124,17 +136,13 @@ struct BwdCfg {
   static constexpr int CH = D / 8;
   static constexpr int QT = BQ * D * 2;         // bytes of one Q or dO tile
   static constexpr int LOADS = QT / (NW * 1024);
-  static constexpr int STAGE = 2 * QT + 2 * BQ * 4;  // Q, dO, LSE, delta
-  static constexpr int KT = BKC * DO * 2;       // resident K columns (dQ operand)
-  static constexpr int KLOADS = KT / (NW * 1024);
-  static constexpr int DSS = BQ + 8;            // dS^T row stride (bf16), padded
-  static constexpr int DS = BKC * DSS * 2;
+  static constexpr int STAGE = 2 * QT + 2 * BQ * 4;  // Q, dO, LSE2, delta
   static constexpr int LIST = 1024;
-  static constexpr int LOADS_PER_STEP = 2 * LOADS + 1;   // per wave (wave 0/1 add lse/delta)
+  static constexpr int LOADS_PER_STEP = 2 * LOADS + 1;   // waves 0/1 add LSE2 / delta
 };
 
 // Chunk swizzle shared by row reads (32 rows, one chunk) and transposed reads
-// (8 rows x 4 chunks) of the Q, dO and K tiles.
+// (8 rows x 4 chunks) of the Q and dO tiles.
 template <int W>
 __device__ inline int swz(int row) {
   if constexpr (W >= 128) return 4 * (row & 3) + ((row >> 2) & 3);
@@ -148,12 +156,10 @@ __device__ inline const FM_LDS char* tile_addr(const FM_LDS char* base, int row,
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char ktile[C::KT];
-  __shared__ __attribute__((aligned(16))) bf16 dsT[C::BKC * C::DSS];
   __shared__ int list[C::LIST];
   __shared__ int wsum[C::NW];
   __shared__ unsigned wcount[3];
@@ -183,18 +189,9 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + slice * D, tbytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + slice * D, tbytes);
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const bf16*>(p.dout) + slice * D, tbytes);
-  const __amdgpu_buffer_rsrc_t rlse = make_rsrc(p.lse + slice, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t rlse = make_rsrc(p.lse2 + slice, (uint32_t)N * 4);
   const __amdgpu_buffer_rsrc_t rdel = make_rsrc(p.delta + slice, (uint32_t)N * 4);
 
-  // K columns [col0, col0 + DO) of the workgroup's keys into LDS (dQ
-  // operand); rows past N read as zero
-#pragma unroll
-  for (int u = 0; u < C::KLOADS; ++u) {
-    const int g = (w * C::KLOADS + u) * 64 + lane;
-    const int row = g / (C::DO / 8), pch = g % (C::DO / 8);
-    load_lds16(rk, (FM_LDS char*)ktile + (w * C::KLOADS + u) * 1024,
-               (uint32_t)((c0 + row) * D + col0 + 8 * (pch ^ swz<C::DO>(row))) * 2);
-  }
   // K and V of this lane's key as the B operands of S = Q K^T and dP = dO V^T
   bf16x8 kB[D / 16], vB[D / 16];
 #pragma unroll
@@ -215,6 +212,8 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
       k_ute = p.ute[vrow + j];
     }
   }
+  const bool causal = p.causal != 0;
+  const bool key_out = j >= N;
 
   f32x16 dvacc[C::DO / 32], dkacc[C::DO / 32];
 #pragma unroll
@@ -238,21 +237,22 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
       load_lds16(rq, st + (w * C::LOADS + u) * 1024, off);
       load_lds16(rdo, st + C::QT + (w * C::LOADS + u) * 1024, off);
     }
-    // 64 LSE values then 64 delta values: 16 lanes x 16 bytes each
-    if (w < 2 && lane < 16)
-      load_lds16(w == 0 ? rlse : rdel, st + 2 * C::QT + w * 256, (uint32_t)(q0 + 4 * lane) * 4);
+    // BQ base-2 LSE values then BQ delta values, 16 bytes per lane
+    if (w < 2 && lane < C::BQ / 4)
+      load_lds16(w == 0 ? rlse : rdel, st + 2 * C::QT + w * C::BQ * 4, (uint32_t)(q0 + 4 * lane) * 4);
   };
 
   auto compute = [&](unsigned entry, auto stage_c) {
     constexpr int S = decltype(stage_c)::value;
+    const int wc = (int)((entry >> (24 + 2 * w)) & 3u);
+    if (wc == 0) return;
     const FM_LDS char* qst = (const FM_LDS char*)(S ? stage1 : stage0);
     const FM_LDS char* dost = qst + C::QT;
     const FM_LDS float* lse_l = (const FM_LDS float*)(qst + 2 * C::QT);
     const FM_LDS float* del_l = lse_l + C::BQ;
     const int q0 = (int)(entry & 0xFFFFFFu) * C::BQ;
-    const int wc = (int)((entry >> (24 + 2 * w)) & 3u);
     bf16x8 pB[C::BQ / 16], dsB[C::BQ / 16];
-    if (wc != 0) {
+    {
       f32x16 sacc[C::BQ / 32], dpacc[C::BQ / 32];
 #pragma unroll
       for (int ib = 0; ib < C::BQ / 32; ++ib) {
@@ -261,13 +261,8 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
         const int row = 32 * ib + l32;
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
-          const bf16x8 a = lds_read_b128(tile_addr<D>(qst, row, 16 * c + 8 * hh));
-          sacc[ib] = mfma32(a, kB[c], sacc[ib]);
-        }
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          const bf16x8 a = lds_read_b128(tile_addr<D>(dost, row, 16 * c + 8 * hh));
-          dpacc[ib] = mfma32(a, vB[c], dpacc[ib]);
+          sacc[ib] = mfma32(lds_read_b128(tile_addr<D>(qst, row, 16 * c + 8 * hh)), kB[c], sacc[ib]);
+          dpacc[ib] = mfma32(lds_read_b128(tile_addr<D>(dost, row, 16 * c + 8 * hh)), vB[c], dpacc[ib]);
         }
       }
 #pragma unroll
@@ -283,91 +278,32 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
             const int i = q0 + rl + e;
             float s = sacc[ib][r];
             if (wc == 1) {
-              bool m = (i >= N) || (j >= N) || (p.causal && j > i);
-              m = m || (k_lts <= i && i < k_lte) || (k_uts <= i && i < k_ute);
-              if (m) s = kNegInf;
+              // bitwise (not short-circuit) so this stays a straight-line select
+              const bool m = (i >= N) | key_out | (causal & (j > i)) |
+                             ((k_lts <= i) & (i < k_lte)) | ((k_uts <= i) & (i < k_ute));
+              s = m ? kNegInf : s;
             }
-            // fully masked rows have LSE = -inf: their P is 0
-            const float l2 = lse4[e] == kNegInf ? __builtin_inff() : lse4[e] * kLog2e;
-            const float pv = fast_exp2(__builtin_fmaf(s, p.sl2, -l2));
-            const float ds = pv * (dpacc[ib][r] - del4[e]) * p.scale;
+            // P = exp2(S * scale * log2e - LSE2); fully masked rows have LSE2 = +inf
+            const float pv = fast_exp2(__builtin_fmaf(s, p.sl2, -lse4[e]));
             pB[2 * ib + r / 8][r % 8] = (bf16)pv;
-            dsB[2 * ib + r / 8][r % 8] = (bf16)ds;
+            dsB[2 * ib + r / 8][r % 8] = (bf16)(pv * (dpacc[ib][r] - del4[e]));
           }
         }
       }
-    } else {
-#pragma unroll
-      for (int c = 0; c < C::BQ / 16; ++c) {
-        pB[c] = bf16x8{};
-        dsB[c] = bf16x8{};
-      }
     }
-    // dS^T to LDS: row = key (this lane's), 4 consecutive query rows per store
-    {
-      bf16* row_ptr = dsT + (C::KW * w + l32) * C::DSS;
+    // dV += P^T dO and dK += dS^T Q; dO / Q operands by transposed reads
+    const int sl = lane & 15;
 #pragma unroll
-      for (int c = 0; c < C::BQ / 16; ++c) {
-        // chunk c holds rows 16c + 4h + 0..3 (elements 0..3) and 16c + 8 + 4h + 0..3
-        const bf16x4 lo = __builtin_shufflevector(dsB[c], dsB[c], 0, 1, 2, 3);
-        const bf16x4 hi = __builtin_shufflevector(dsB[c], dsB[c], 4, 5, 6, 7);
-        *reinterpret_cast<FM_LDS bf16x4*>((FM_LDS bf16*)row_ptr + 16 * c + 4 * hh) = lo;
-        *reinterpret_cast<FM_LDS bf16x4*>((FM_LDS bf16*)row_ptr + 16 * c + 8 + 4 * hh) = hi;
-      }
-    }
-    if (wc != 0) {
-      // dV += P^T dO and dK += dS^T Q; dO / Q operands by transposed reads
-      const int sl = lane & 15;
+    for (int c = 0; c < C::BQ / 16; ++c) {
+      const int ra = 16 * c + 4 * hh + (sl >> 2);
+      const int rb = ra + 8;
 #pragma unroll
-      for (int c = 0; c < C::BQ / 16; ++c) {
-        const int ra = 16 * c + 4 * hh + (sl >> 2);
-        const int rb = ra + 8;
-#pragma unroll
-        for (int mb = 0; mb < C::DO / 32; ++mb) {
-          const int col = col0 + 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
-          const bf16x8 bo = cat(lds_read_tr(tile_addr<D>(dost, ra, col)), lds_read_tr(tile_addr<D>(dost, rb, col)));
-          dvacc[mb] = mfma32(pB[c], bo, dvacc[mb]);
-          const bf16x8 bq = cat(lds_read_tr(tile_addr<D>(qst, ra, col)), lds_read_tr(tile_addr<D>(qst, rb, col)));
-          dkacc[mb] = mfma32(dsB[c], bq, dkacc[mb]);
-        }
-      }
-    }
-    lds_barrier();
-    // dQ over all 128 keys: the step's (BQ/32) x (D/32) output blocks of 32x32
-    // are split evenly over the waves; a wave's blocks share one row block.
-    {
-      constexpr int BPW = (C::BQ / 32) * (C::DO / 32) / C::NW;
-      const int ob0 = w * BPW;
-      const int ib = ob0 / (C::DO / 32);
-      const int sl = lane & 15;
-      f32x16 dq[BPW];
-#pragma unroll
-      for (int t = 0; t < BPW; ++t) dq[t] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < C::BKC / 16; ++c) {
-        // A: dS[i][16c + 8h + e] from dS^T (row = key, column = query)
-        const int kr = 16 * c + 8 * hh + (sl >> 2);
-        const int qcol = 32 * ib + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
-        const FM_LDS bf16* d0 = (const FM_LDS bf16*)dsT + kr * C::DSS + qcol;
-        const bf16x8 a = cat(lds_read_tr(d0), lds_read_tr(d0 + 4 * C::DSS));
-#pragma unroll
-        for (int t = 0; t < BPW; ++t) {
-          const int mb = (ob0 + t) % (C::DO / 32);
-          const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
-          const bf16x8 bk = cat(lds_read_tr(tile_addr<C::DO>((const FM_LDS char*)ktile, kr, col)),
-                                lds_read_tr(tile_addr<C::DO>((const FM_LDS char*)ktile, kr + 4, col)));
-          dq[t] = mfma32(a, bk, dq[t]);
-        }
-      }
-      // add into the float32 accumulator (lane holds column 32mb + lane % 32)
-#pragma unroll
-      for (int t = 0; t < BPW; ++t) {
-        const int mb = (ob0 + t) % (C::DO / 32);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = q0 + 32 * ib + 8 * (r / 4) + 4 * hh + (r % 4);
-          if (i < N) unsafeAtomicAdd(p.dq_acc + (slice + i) * D + col0 + 32 * mb + l32, dq[t][r]);
-        }
+      for (int mb = 0; mb < C::DO / 32; ++mb) {
+        const int col = col0 + 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+        const bf16x8 bo = cat(lds_read_tr(tile_addr<D>(dost, ra, col)), lds_read_tr(tile_addr<D>(dost, rb, col)));
+        dvacc[mb] = mfma32(pB[c], bo, dvacc[mb]);
+        const bf16x8 bq = cat(lds_read_tr(tile_addr<D>(qst, ra, col)), lds_read_tr(tile_addr<D>(qst, rb, col)));
+        dkacc[mb] = mfma32(dsB[c], bq, dkacc[mb]);
       }
     }
   };
@@ -394,7 +330,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
     bool valid = false;
     if (qb < p.nqb) {
       const int r0 = qb * C::BQ, r1 = min(N, r0 + C::BQ);
-      const int wgc = tile_class(kbnd, r0, r1, c0, c1, p.causal != 0);
+      const int wgc = tile_class(kbnd, r0, r1, c0, c1, causal);
       cnt0 += wgc == 0;
       cnt1 += wgc == 1;
       cnt2 += wgc == 2;
@@ -408,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
           int cls = 0;
           if (a0 < N) {
             const BlockBounds wb = load_bounds(table + (long long)(a0 / 64) * 8);
-            cls = tile_class(wb, r0, r1, a0, min(N, a0 + C::KW), p.causal != 0);
+            cls = tile_class(wb, r0, r1, a0, min(N, a0 + C::KW), causal);
             if (ragged && cls == 2) cls = 1;
           }
           bits |= cls << (2 * ww);
@@ -436,7 +372,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
         const unsigned entry_it = (unsigned)list[it];
         if (it + 1 < cnt) {
           issue((unsigned)list[it + 1], std::integral_constant<int, 1 - S>{});
-          // waves 0 and 1 issued one more load (LSE / delta)
+          // waves 0 and 1 issued one more load (LSE2 / delta)
           if (w < 2) wait_vmcnt<C::LOADS_PER_STEP>();
           else wait_vmcnt<C::LOADS_PER_STEP - 1>();
         } else {
@@ -456,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
   }
 
   wait_vmcnt<0>();  // no load into LDS may still be in flight when the wave ends
-  // --- write dK (already scaled) and dV for this wave's keys
+  // --- write dK = scale * dS^T Q and dV for this wave's keys
   if (wc0 < N) {
     bf16* dkg = reinterpret_cast<bf16*>(p.dk) + slice * D;
     bf16* dvg = reinterpret_cast<bf16*>(p.dv) + slice * D;
@@ -466,7 +402,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
       for (int r = 0; r < 16; ++r) {
         const int key = wc0 + 8 * (r / 4) + 4 * hh + (r % 4);
         if (key < N) {
-          dkg[(long long)key * D + col0 + 32 * mb + l32] = (bf16)dkacc[mb][r];
+          dkg[(long long)key * D + col0 + 32 * mb + l32] = (bf16)(dkacc[mb][r] * p.scale);
           dvg[(long long)key * D + col0 + 32 * mb + l32] = (bf16)dvacc[mb][r];
         }
       }
@@ -575,8 +511,7 @@ __global__ __launch_bounds__(256, 1) void bwd_f32_kernel(BwdParams p) {
     }
     if (tid < BQ) {
       const bool ok = q0 + tid < N;
-      const float l = ok ? p.lse[slice + q0 + tid] : 0.f;
-      lse_s[tid] = l == kNegInf ? __builtin_inff() : l * kLog2e;
+      lse_s[tid] = ok ? p.lse2[slice + q0 + tid] : __builtin_inff();
       del_s[tid] = ok ? p.delta[slice + q0 + tid] : 0.f;
     }
     __syncthreads();
@@ -669,15 +604,15 @@ static hipError_t launch_convert(const BwdParams& p, int d, hipStream_t stream) 
 }
 
 template <int D>
-static hipError_t launch_bwd_bf16(BwdParams p, hipStream_t stream) {
+static hipError_t launch_bwd_bf16(BwdParams p, const AttnArgs& a, hipStream_t stream) {
   p.nqb = (p.N + BwdCfg<D>::BQ - 1) / BwdCfg<D>::BQ;
   hipError_t e = launch_pre<D, bf16>(p, stream);
   if (e != hipSuccess) return e;
-  const long long grid = (long long)p.B * p.H * p.nkb * BwdCfg<D>::NSPLIT;
-  hipLaunchKernelGGL(bwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
-  e = hipGetLastError();
+  e = launch_bwd_dq(a, p.lse2, stream);
   if (e != hipSuccess) return e;
-  return launch_convert<bf16>(p, D, stream);
+  const long long grid = (long long)p.B * p.H * p.nkb * BwdCfg<D>::NSPLIT;
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -707,6 +642,7 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.table = a.table;
   p.dq_acc = a.dq_acc;
   p.delta = a.delta;
+  p.lse2 = a.lse2;
   p.dq = a.dq;
   p.dk = a.dk;
   p.dv = a.dv_out;
@@ -725,9 +661,9 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.nkb64 = (a.N + kTableBlock - 1) / kTableBlock;
   if (a.is_bf16) {
     switch (a.d) {
-      case 64: return launch_bwd_bf16<64>(p, stream);
-      case 128: return launch_bwd_bf16<128>(p, stream);
-      case 256: return launch_bwd_bf16<256>(p, stream);
+      case 64: return launch_bwd_bf16<64>(p, a, stream);
+      case 128: return launch_bwd_bf16<128>(p, a, stream);
+      case 256: return launch_bwd_bf16<256>(p, a, stream);
     }
   } else {
     switch (a.d) {

@@ -99,6 +99,15 @@ __device__ inline f32x16 mfma32f(float a, float b, f32x16 c) {
 // ---------------------------------------------------------------- math
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + sum of the 8 bf16 values of v, two per v_dot2_f32_bf16
+__device__ inline float sum8_bf16(bf16x8 v, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[e], v[e + 1]}, one, acc, false);
+  return acc;
+}
+
 __device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // ---------------------------------------------------------------- mask rule

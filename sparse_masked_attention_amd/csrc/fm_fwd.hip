@@ -40,6 +40,11 @@ struct FwdParams {
   void* o;
   float* lse;
   unsigned long long* counts;
+  // dQ mode (backward): dO, the base-2 logsumexp and delta per row, dQ out
+  const void* dout;
+  const float* lse2;
+  const float* delta;
+  void* dq;
   int B, H, N, hm, causal;
   int has_lt, has_lte, has_ut;
   float scale, sl2;
@@ -74,11 +79,26 @@ __device__ inline void mask_block(f32x16& s, const FM_LDS int* vl, int kl0, int 
 }
 
 // ---------------------------------------------------------------- bf16 kernel
-template <int D>
-struct FwdCfg {
+// One query-major kernel serves two passes:
+//   MODE 0, forward: O and LSE with online softmax;
+//   MODE 1, the dQ pass of the backward: with the forward's LSE and
+//     delta = rowsum(dO * O) known per row, P = exp(S - LSE) and
+//     dS = P * (dO V^T - delta) need no running state, and
+//     dQ^T += K^T dS^T takes the place of O^T += V^T P^T.
+// Both stream K/V tiles through LDS with the same classification, scan and
+// pipeline; each wave owns 32 query rows (its lanes hold one row each in the
+// transposed score layout S^T = K Q^T).
+constexpr int kModeFwd = 0;
+constexpr int kModeDq = 1;
+
+template <int D, int MODE>
+struct QCfg {
   static constexpr int NW = 4;
-  static constexpr int BR = 32 * NW;
-  static constexpr int BC = 64;
+  static constexpr int WR = 32;                           // query rows per wave
+  static constexpr int BR = WR * NW;                      // query rows per workgroup
+  static constexpr int BC = 64;                           // keys per tile
+  // 32-key blocks per inner step (1 keeps registers within budget)
+  static constexpr int JBS = (D >= 256 || MODE == kModeDq) ? 1 : 2;
   static constexpr int CH = D / 8;                        // 16-byte chunks per row
   static constexpr int TILE = BC * D * 2;                 // bytes of one K or V tile
   static constexpr int LOADS = TILE / (NW * 1024);        // per wave per tensor
@@ -88,22 +108,26 @@ struct FwdCfg {
   static constexpr int LOADS_PER_TILE = 2 * LOADS + 1;    // per wave
 };
 
-// XOR swizzles of the 16-byte chunk index, chosen per tile so that the MFMA
-// operand reads (K: 32 rows at one chunk; V: transposed 8-row blocks) spread
-// over the LDS banks.
+// XOR swizzle of the 16-byte chunk index within a row: 32 consecutive rows
+// read at one chunk (row operand reads) and 8 rows x 4 chunks (transposed
+// reads) both spread over the LDS banks.
 template <int D>
-__device__ inline int swz_k(int row) { return row & ((D / 8 < 16 ? D / 8 : 16) - 1); }
-template <int D>
-__device__ inline int swz_v(int row) {
-  if constexpr (D == 64) return 4 * ((row >> 1) & 1);
-  else return 4 * (row & 3);
+__device__ inline int fswz(int row) {
+  if constexpr (D >= 128) return 4 * (row & 3) + ((row >> 2) & 3);
+  else return 4 * (row & 1) + ((row >> 1) & 3);
 }
 
-template <int D>
-__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_bf16_kernel(FwdParams p) {
-  using C = FwdCfg<D>;
-  // Two pipeline stages as separate LDS objects, so the compiler can tell
-  // that reads of one stage do not depend on the loads landing in the other.
+// Running-max slack, in log2 units: the max used to scale P only moves when
+// a row's new max exceeds it by more than this, so the O rescale is rare;
+// P then stays below 2^8, well inside bf16 and fp32 range. Exact either way,
+// since O and the row sum always use the same offset.
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdParams p) {
+  using C = QCfg<D, MODE>;
+  constexpr bool DQ = MODE == kModeDq;
+  // Two pipeline stages as separate LDS objects.
   __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
   __shared__ int list[C::LIST];
@@ -114,21 +138,23 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
   const int lane = tid & 63;
   const int w = uniform(tid >> 6);
   const int hh = lane >> 5;
+  const int l32 = lane & 31;
   const int BH = p.B * p.H;
   const int bh = blockIdx.x % BH;
-  const int qb = p.nqb - 1 - (int)(blockIdx.x / BH);
+  const int qb = p.nqb - 1 - (int)(blockIdx.x / BH);   // heavy (late) query blocks first
   const int b = bh / p.H, h = bh % p.H;
   const int hmi = p.hm == 1 ? 0 : h;
   const int N = p.N;
   const long long slice = (long long)bh * N;
   const int r0 = qb * C::BR;
   const int r1 = min(N, r0 + C::BR);
-  const int i = r0 + 32 * w + (lane & 31);
+  const int wr0 = r0 + C::WR * w;                       // this wave's first row
+  const int i = wr0 + l32;                              // this lane's row
+  const uint32_t tbytes = (uint32_t)N * D * 2;
 
-  const bf16* qg = reinterpret_cast<const bf16*>(p.q) + slice * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + slice * D, (uint32_t)N * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + slice * D, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(p.q) + slice * D, tbytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + slice * D, tbytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + slice * D, tbytes);
   const long long vrow = ((long long)b * p.hm + hmi) * N;
   const int32_t* vecs[4] = {p.lts, p.lte, p.uts, p.ute};
   // each wave stages one of the four boundary vectors (absent ones read as 0)
@@ -137,14 +163,26 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
   const __amdgpu_buffer_rsrc_t rvec =
       make_rsrc(vec_present ? my_vec + vrow : p.table, vec_present ? (uint32_t)N * 4 : 0u);
 
-  // Q rows of this lane as the B operand of S^T = K Q^T: chunk c holds
-  // Q[i][16c + 8h .. 16c + 8h + 7]. Rows past N read as zero.
+  // This lane's row of Q (and dO) as B operands: chunk c holds
+  // [i][16c + 8h .. +7]. Rows past N read as zero.
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c)
     qf[c] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(i * D + 16 * c + 8 * hh) * 2));
+  bf16x8 dof[DQ ? D / 16 : 1];
+  float row_lse2 = 0.f, row_delta = 0.f;
+  if constexpr (DQ) {
+    const __amdgpu_buffer_rsrc_t rdo =
+        make_rsrc(reinterpret_cast<const bf16*>(p.dout) + slice * D, tbytes);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      dof[c] = __builtin_bit_cast(bf16x8, buffer_load16(rdo, (uint32_t)(i * D + 16 * c + 8 * hh) * 2));
+    // fully masked rows carry +inf here, so their P is 0
+    row_lse2 = i < N ? p.lse2[slice + i] : __builtin_inff();
+    row_delta = i < N ? p.delta[slice + i] : 0.f;
+  }
 
-  f32x16 oacc[D / 32];
+  f32x16 oacc[D / 32];           // O^T (forward) or dQ^T (dQ pass)
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
@@ -152,6 +190,8 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
   if (tid < 3) wcount[tid] = 0;
   unsigned cnt0 = 0, cnt1 = 0, cnt2 = 0;
   const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb * 8;
+  const bool causal = p.causal != 0, has_lt = p.has_lt != 0, has_lte = p.has_lte != 0,
+             has_ut = p.has_ut != 0;
 
   // --- issue the loads of one key tile into a stage
   auto issue = [&](unsigned entry, auto stage_c) {
@@ -162,18 +202,28 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
     for (int u = 0; u < C::LOADS; ++u) {
       const int g = (w * C::LOADS + u) * 64 + lane;   // physical chunk in the tile
       const int row = g / C::CH, pch = g % C::CH;
-      const uint32_t ko = (uint32_t)((kbase + row) * D + 8 * (pch ^ swz_k<D>(row))) * 2;
-      load_lds16(rk, st + (w * C::LOADS + u) * 1024, ko);
-    }
-#pragma unroll
-    for (int u = 0; u < C::LOADS; ++u) {
-      const int g = (w * C::LOADS + u) * 64 + lane;
-      const int row = g / C::CH, pch = g % C::CH;
-      const uint32_t vo = (uint32_t)((kbase + row) * D + 8 * (pch ^ swz_v<D>(row))) * 2;
-      load_lds16(rv, st + C::TILE + (w * C::LOADS + u) * 1024, vo);
+      const uint32_t off = (uint32_t)((kbase + row) * D + 8 * (pch ^ fswz<D>(row))) * 2;
+      load_lds16(rk, st + (w * C::LOADS + u) * 1024, off);
+      load_lds16(rv, st + C::TILE + (w * C::LOADS + u) * 1024, off);
     }
     // 16 lanes x 16 bytes = one 64-key vector per wave
     if (lane < 16) load_lds16(rvec, st + 2 * C::TILE + w * 256, (uint32_t)(kbase + 4 * lane) * 4);
+  };
+
+  // row operand read (32 rows of a tile at one 16-byte chunk)
+  auto row_read = [&](const FM_LDS char* t, int row, int chunk) {
+    return lds_read_b128(t + row * D * 2 + ((chunk ^ fswz<D>(row)) << 4));
+  };
+  // transposed operand read: for MFMA contraction chunk c (16 keys) and
+  // column block mb, 4 consecutive keys of one column per lane, twice
+  auto tr_read = [&](const FM_LDS char* t, int c, int mb) {
+    const int sl = lane & 15;
+    const int row_a = 16 * c + 4 * hh + (sl >> 2);
+    const int row_b = row_a + 8;
+    const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+    const FM_LDS char* pa = t + row_a * D * 2 + (((col >> 3) ^ fswz<D>(row_a)) << 4) + (col & 7) * 2;
+    const FM_LDS char* pb = t + row_b * D * 2 + (((col >> 3) ^ fswz<D>(row_b)) << 4) + (col & 7) * 2;
+    return cat(lds_read_tr(pa), lds_read_tr(pb));
   };
 
   // --- one key tile of work for this wave
@@ -185,65 +235,97 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
     const FM_LDS char* kst = (const FM_LDS char*)(S ? stage1 : stage0);
     const FM_LDS char* vst = kst + C::TILE;
     const FM_LDS int* vl = (const FM_LDS int*)(kst + 2 * C::TILE);
-
-    f32x16 s[C::BC / 32];
+    constexpr int JBS = C::JBS;
 #pragma unroll
-    for (int jb = 0; jb < C::BC / 32; ++jb) {
-      s[jb] = f32x16{};
-      const int row = jb * 32 + (lane & 31);
+    for (int hk = 0; hk < C::BC / 32 / JBS; ++hk) {
+      // S^T = K Q^T (and dP^T = V dO^T in the dQ pass)
+      f32x16 s[JBS], dp[DQ ? JBS : 1];
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 a = lds_read_b128(kst + row * D * 2 + ((2 * c + hh) ^ swz_k<D>(row)) * 16);
-        s[jb] = mfma32(a, qf[c], s[jb]);
+      for (int jj = 0; jj < JBS; ++jj) {
+        const int row = (hk * JBS + jj) * 32 + l32;
+        s[jj] = f32x16{};
+        if constexpr (DQ) dp[jj] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          s[jj] = mfma32(row_read(kst, row, 2 * c + hh), qf[c], s[jj]);
+          if constexpr (DQ) dp[jj] = mfma32(row_read(vst, row, 2 * c + hh), dof[c], dp[jj]);
+        }
       }
-    }
-    if (wc == 1) {
+      if (wc == 1) {
+        // element test against the tile's staged bounds
 #pragma unroll
-      for (int jb = 0; jb < C::BC / 32; ++jb) mask_block(s[jb], vl, jb * 32, kbase, i, p, hh);
-    }
-    // online softmax (base-2 exponent with the scale folded in)
-    float mx = kNegInf;
+        for (int jj = 0; jj < JBS; ++jj)
 #pragma unroll
-    for (int jb = 0; jb < C::BC / 32; ++jb)
+          for (int g = 0; g < 4; ++g) {
+            const int kl = (hk * JBS + jj) * 32 + 8 * g + 4 * hh;
+            const i32x4 lts4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 0 * 64 + kl);
+            const i32x4 lte4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 1 * 64 + kl);
+            // absent vectors were staged as zeros, and has_* gates their use
+            const i32x4 uts4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 2 * 64 + kl);
+            const i32x4 ute4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 3 * 64 + kl);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * p.sl2);
-    const float msl = m_use * p.sl2;
-    float rs = 0.f;
-    bf16x8 pf[C::BC / 16];
-#pragma unroll
-    for (int jb = 0; jb < C::BC / 32; ++jb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(__builtin_fmaf(s[jb][r], p.sl2, -msl));
-        rs += pv;
-        pf[2 * jb + r / 8][r % 8] = (bf16)pv;
+            for (int e = 0; e < 4; ++e) {
+              const int j = kbase + kl + e;
+              const int lte_v = has_lte ? lte4[e] : N;
+              // bitwise (not short-circuit) so this stays a straight-line select
+              const bool m = (j >= N) | (causal & (j > i)) |
+                             (has_lt & (lts4[e] <= i) & (i < lte_v)) |
+                             (has_ut & (uts4[e] <= i) & (i < ute4[e]));
+              s[jj][4 * g + e] = m ? kNegInf : s[jj][4 * g + e];
+            }
+          }
       }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
+      bf16x8 pf[2 * JBS];
+      if constexpr (!DQ) {
+        float mx = kNegInf;
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
-    // O^T += V^T P^T; V^T chunks via transposed reads of the row-major tile
-    const int sl = lane & 15;
+        for (int jj = 0; jj < JBS; ++jj)
 #pragma unroll
-    for (int c = 0; c < C::BC / 16; ++c) {
-      const int row_a = 16 * c + 4 * hh + (sl >> 2);
-      const int row_b = row_a + 8;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jj][r]);
+        mx = fmaxf(mx, xor32(mx));
+        // move the offset (and rescale O and the sum) only when some row's max
+        // outgrew it by more than the slack; a row with nothing open keeps -inf
+        if (__ballot((mx - m_run) * p.sl2 > kRescaleSlack) != 0) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = m_new == kNegInf ? 1.f : fast_exp2((m_run - m_new) * p.sl2);
+          l_run *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) {
-        const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
-        const FM_LDS char* pa = vst + row_a * D * 2 + (((col >> 3) ^ swz_v<D>(row_a)) << 4) + (col & 7) * 2;
-        const FM_LDS char* pb = vst + row_b * D * 2 + (((col >> 3) ^ swz_v<D>(row_b)) << 4) + (col & 7) * 2;
-        const bf16x8 a = cat(lds_read_tr(pa), lds_read_tr(pb));
-        oacc[mb] = mfma32(a, pf[c], oacc[mb]);
+          for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+          m_run = m_new;
+        }
+        const float msl = (m_run == kNegInf ? 0.f : m_run) * p.sl2;
+#pragma unroll
+        for (int jj = 0; jj < JBS; ++jj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            pf[2 * jj + r / 8][r % 8] = (bf16)fast_exp2(__builtin_fmaf(s[jj][r], p.sl2, -msl));
+        // row sum of the rounded probabilities (the values the PV MFMA
+        // uses), two per v_dot2_f32_bf16
+        float rs = l_run;
+#pragma unroll
+        for (int c = 0; c < 2 * JBS; ++c) rs = sum8_bf16(pf[c], rs);
+        l_run = rs;
+      } else {
+        // dS = P * (dP - delta) with P = exp2(S * scale * log2e - LSE2)
+#pragma unroll
+        for (int jj = 0; jj < JBS; ++jj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pv = fast_exp2(__builtin_fmaf(s[jj][r], p.sl2, -row_lse2));
+            pf[2 * jj + r / 8][r % 8] = (bf16)(pv * (dp[jj][r] - row_delta));
+          }
+      }
+      // O^T += V^T P^T (forward) or dQ^T += K^T dS^T (dQ pass)
+#pragma unroll
+      for (int cc = 0; cc < 2 * JBS; ++cc) {
+        const int c = 2 * JBS * hk + cc;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32(tr_read(DQ ? kst : vst, c, mb), pf[cc], oacc[mb]);
       }
     }
   };
 
-  // --- scan the key blocks, compact the visited ones, process in chunks
+  // --- scan the key blocks, compact the visible ones, process in chunks
   int cnt = 0;
   for (int base = 0; base < p.nkb; base += 256) {
     const int kb = base + tid;
@@ -252,7 +334,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
     if (kb < p.nkb) {
       const BlockBounds bb = load_bounds(table + (long long)kb * 8);
       const int c0 = kb * C::BC, c1 = min(N, c0 + C::BC);
-      const int wgc = tile_class(bb, r0, r1, c0, c1, p.causal != 0);
+      const int wgc = tile_class(bb, r0, r1, c0, c1, causal);
       cnt0 += wgc == 0;
       cnt1 += wgc == 1;
       cnt2 += wgc == 2;
@@ -262,10 +344,10 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
         int bits = 0;
 #pragma unroll
         for (int ww = 0; ww < C::NW; ++ww) {
-          const int a0 = r0 + 32 * ww;
+          const int a0 = r0 + C::WR * ww;
           int cls = 0;
           if (a0 < N) {
-            cls = tile_class(bb, a0, min(N, a0 + 32), c0, c1, p.causal != 0);
+            cls = tile_class(bb, a0, min(N, a0 + C::WR), c0, c1, causal);
             if (ragged && cls == 2) cls = 1;
           }
           bits |= cls << (2 * ww);
@@ -311,21 +393,38 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fwd_bf16_kernel(FwdPara
     }
   }
 
-  // --- epilogue: normalise, store O (bf16) and the natural-log LSE
-  const float lt = l_run + xor32(l_run);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (i < N) {
-    bf16* og = reinterpret_cast<bf16*>(p.o) + (slice + i) * D;
+  // --- epilogue
+  if constexpr (!DQ) {
+    // normalise, store O (bf16) and the natural-log LSE
+    const float lt = l_run + xor32(l_run);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (i < N) {
+      bf16* og = reinterpret_cast<bf16*>(p.o) + (slice + i) * D;
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb)
+      for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v4;
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[mb][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(og + 32 * mb + 8 * g + 4 * hh) = v4;
-      }
-    if (hh == 0) p.lse[slice + i] = lt > 0.f ? m_run * p.scale + __logf(lt) : kNegInf;
+          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[mb][4 * g + e] * inv);
+          *reinterpret_cast<bf16x4*>(og + 32 * mb + 8 * g + 4 * hh) = v4;
+        }
+      if (hh == 0) p.lse[slice + i] = lt > 0.f ? m_run * p.scale + __logf(lt) : kNegInf;
+    }
+  } else {
+    // dQ = scale * dS K
+    if (i < N) {
+      bf16* dqg = reinterpret_cast<bf16*>(p.dq) + (slice + i) * D;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[mb][4 * g + e] * p.scale);
+          *reinterpret_cast<bf16x4*>(dqg + 32 * mb + 8 * g + 4 * hh) = v4;
+        }
+    }
   }
   if (p.counts != nullptr) {
     atomicAdd(&wcount[0], cnt0);
@@ -471,15 +570,18 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------- launch
-template <int D>
-static hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
+template <int D, int MODE>
+static hipError_t launch_qmajor(FwdParams p, hipStream_t stream) {
+  using C = QCfg<D, MODE>;
+  p.nqb = (p.N + C::BR - 1) / C::BR;
   const long long grid = (long long)p.B * p.H * p.nqb;
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((qmajor_bf16_kernel<D, MODE>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream) {
+static hipError_t launch_fwd_f32(FwdParams p, hipStream_t stream) {
+  p.nqb = (p.N + 127) / 128;
   const long long grid = (long long)p.B * p.H * p.nqb;
   hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -508,19 +610,56 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
   p.has_ut = !a.mask.causal && a.mask.uts != nullptr && a.mask.ute != nullptr;
   p.scale = a.scale;
   p.sl2 = a.scale * kLog2e;
-  p.nqb = (a.N + kFwdBlockQ - 1) / kFwdBlockQ;
   p.nkb = (a.N + kFwdBlockK - 1) / kFwdBlockK;
   if (a.is_bf16) {
     switch (a.d) {
-      case 64: return launch_fwd_bf16<64>(p, stream);
-      case 128: return launch_fwd_bf16<128>(p, stream);
-      case 256: return launch_fwd_bf16<256>(p, stream);
+      case 64: return launch_qmajor<64, kModeFwd>(p, stream);
+      case 128: return launch_qmajor<128, kModeFwd>(p, stream);
+      case 256: return launch_qmajor<256, kModeFwd>(p, stream);
     }
   } else {
     switch (a.d) {
       case 64: return launch_fwd_f32<64>(p, stream);
       case 128: return launch_fwd_f32<128>(p, stream);
     }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fm
+
+namespace fm {
+
+// dQ pass of the backward (query-major; see qmajor_bf16_kernel).
+hipError_t launch_bwd_dq(const AttnArgs& a, const float* lse2, hipStream_t stream) {
+  FwdParams p{};
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.lts = a.mask.lts;
+  p.lte = a.mask.lte;
+  p.uts = a.mask.uts;
+  p.ute = a.mask.ute;
+  p.table = a.table;
+  p.dout = a.dout;
+  p.lse2 = lse2;
+  p.delta = a.delta;
+  p.dq = a.dq;
+  p.B = a.B;
+  p.H = a.H;
+  p.N = a.N;
+  p.hm = a.mask.hm;
+  p.causal = a.mask.causal;
+  p.has_lt = a.mask.lts != nullptr;
+  p.has_lte = a.mask.lts != nullptr && a.mask.lte != nullptr;
+  p.has_ut = !a.mask.causal && a.mask.uts != nullptr && a.mask.ute != nullptr;
+  p.scale = a.scale;
+  p.sl2 = a.scale * kLog2e;
+  p.nkb = (a.N + kFwdBlockK - 1) / kFwdBlockK;
+  switch (a.d) {
+    case 64: return launch_qmajor<64, kModeDq>(p, stream);
+    case 128: return launch_qmajor<128, kModeDq>(p, stream);
+    case 256: return launch_qmajor<256, kModeDq>(p, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -11,8 +11,9 @@ namespace fm {
 constexpr int kTableBlock = 64;
 
 // Tile shapes the attention kernels classify (query rows x key columns).
-constexpr int kFwdBlockQ = 128;
 constexpr int kFwdBlockK = 64;
+// forward query-block height (4 waves x 32 rows)
+inline int fwd_block_q(int d, int is_bf16) { (void)d; (void)is_bf16; return 128; }
 constexpr int kBwdBlockK = 128;
 // backward query-block height: 64 rows for bf16 with d <= 128, else 32
 inline int bwd_block_q(int d, int is_bf16) { return (is_bf16 && d <= 128) ? 64 : 32; }
@@ -43,8 +44,9 @@ struct AttnArgs {
   void* dq;
   void* dk;
   void* dv_out;
-  float* dq_acc;      // backward workspace: float32 [B, H, N, d]
+  float* dq_acc;      // backward workspace (fp32 path): float32 [B, H, N, d]
   float* delta;       // backward workspace: float32 [B, H, N]
+  float* lse2;        // backward workspace: float32 [B, H, N], base-2 logsumexp
   unsigned long long* tile_counts;
 };
 
@@ -54,5 +56,6 @@ hipError_t launch_classify(const int32_t* table, int B, int hm, int N, int causa
                            int block_k, int8_t* out, hipStream_t stream);
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq(const AttnArgs& a, const float* lse2, hipStream_t stream);
 
 }  // namespace fm

@@ -53,6 +53,8 @@ def test_table_block_and_tile_shapes(lib):
     import torch
     assert _binding.table_block() == 64
     assert _binding.tile_shape(False, 128, torch.bfloat16) == (128, 64)
+    assert _binding.tile_shape(False, 256, torch.bfloat16) == (128, 64)
+    assert _binding.tile_shape(False, 64, torch.float32) == (128, 64)
     assert _binding.tile_shape(True, 128, torch.bfloat16) == (64, 128)
     assert _binding.tile_shape(True, 256, torch.bfloat16) == (32, 128)
     assert _binding.tile_shape(True, 64, torch.float32) == (32, 128)
@@ -65,7 +67,9 @@ def test_workspace_size(lib):
     fwd = _binding.workspace_size(False, 1, 32, 8192, 128, 128, 1, torch.bfloat16)
     assert fwd == 128 * 8 * 4              # the table: 128 key blocks x 8 int32
     bwd = _binding.workspace_size(True, 1, 32, 8192, 128, 128, 1, torch.bfloat16)
-    assert bwd == 4096 + 32 * 8192 * 4 + 32 * 8192 * 128 * 4
+    assert bwd == 4096 + 2 * 32 * 8192 * 4
+    bwd32 = _binding.workspace_size(True, 1, 32, 8192, 128, 128, 1, torch.float32)
+    assert bwd32 == 4096 + 2 * 32 * 8192 * 4 + 32 * 8192 * 128 * 4
     assert _binding.workspace_size(False, 1, 1, 10, 96, 96, 1, torch.bfloat16) == 0
 
 

@@ -102,6 +102,17 @@ def test_tile_counts_d256_and_fp32():
         assert counts.cpu().numpy().tolist() == ref.tolist()
 
 
+def test_bf16_backward_is_deterministic():
+    B, H, N, d = 1, 4, 1500, 128
+    say("bwd determinism")
+    q, k, v, do = qkvo(B, H, N, d, 2700, with_do=True)
+    vec = I.stack_masks([I.make_mask("share_question", N, np.random.default_rng(2))])
+    a = run_case(q, k, v, do, vec)
+    b = run_case(q, k, v, do, vec)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 def test_fully_masked_rows():
     N = 400
     say("bwd empty rows")
