@@ -170,8 +170,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int hh = lane >> 5;
   const int l32 = lane & 31;
   const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
-  const int rest = (int)(blockIdx.x / BH);   // heavy (early) key blocks first
+  int bh, rest;                              // heavy (early) key blocks first
+  xcd_order((int)blockIdx.x, BH, p.nkb * C::NSPLIT, bh, rest);
   const int kb = rest / C::NSPLIT;
   const int sp = rest % C::NSPLIT;           // which output column half
   const int col0 = sp * C::DO;
@@ -212,8 +212,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       k_ute = p.ute[vrow + j];
     }
   }
-  const bool causal = p.causal != 0;
-  const bool key_out = j >= N;
+  const bool causal = p.causal != 0, has_lt = p.has_lt != 0, has_ut = p.has_ut != 0;
 
   f32x16 dvacc[C::DO / 32], dkacc[C::DO / 32];
 #pragma unroll
@@ -265,6 +264,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           dpacc[ib] = mfma32(lds_read_b128(tile_addr<D>(dost, row, 16 * c + 8 * hh)), vB[c], dpacc[ib]);
         }
       }
+      if (wc == 1) {
+#pragma unroll
+        for (int ib = 0; ib < C::BQ / 32; ++ib) {
+          // masked rows of this lane's key among rows q0 + 32 ib + [0, 32)
+          // (rows past N too: their staged LSE is not +inf), shifted so that
+          // bit 8 g + e is the row of register 4 g + e
+          const int rb = q0 + 32 * ib;
+          const uint32_t mw = (key_row_mask(j, rb, N, causal, has_lt, has_ut, k_lts, k_lte, k_uts, k_ute) |
+                               row_bits(N, rb + 32, rb)) >> (4 * hh);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[ib][r] = ((mw >> (8 * (r / 4) + r % 4)) & 1u) ? kNegInf : sacc[ib][r];
+        }
+      }
 #pragma unroll
       for (int ib = 0; ib < C::BQ / 32; ++ib) {
 #pragma unroll
@@ -275,14 +288,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            const int i = q0 + rl + e;
-            float s = sacc[ib][r];
-            if (wc == 1) {
-              // bitwise (not short-circuit) so this stays a straight-line select
-              const bool m = (i >= N) | key_out | (causal & (j > i)) |
-                             ((k_lts <= i) & (i < k_lte)) | ((k_uts <= i) & (i < k_ute));
-              s = m ? kNegInf : s;
-            }
+            const float s = sacc[ib][r];
             // P = exp2(S * scale * log2e - LSE2); fully masked rows have LSE2 = +inf
             const float pv = fast_exp2(__builtin_fmaf(s, p.sl2, -lse4[e]));
             pB[2 * ib + r / 8][r % 8] = (bf16)pv;
@@ -369,7 +375,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     if (cnt > C::LIST - 256 || base + 256 >= p.nqb) {
       auto step = [&](int it, auto stage_c) {
         constexpr int S = decltype(stage_c)::value;
-        const unsigned entry_it = (unsigned)list[it];
+        // uniform across the wave: keeps the class tests scalar branches
+        const unsigned entry_it = uniform_u32((unsigned)list[it]);
         if (it + 1 < cnt) {
           issue((unsigned)list[it + 1], std::integral_constant<int, 1 - S>{});
           // waves 0 and 1 issued one more load (LSE2 / delta)

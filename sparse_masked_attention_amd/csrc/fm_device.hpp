@@ -108,7 +108,76 @@ __device__ inline float sum8_bf16(bf16x8 v, float acc) {
   return acc;
 }
 
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Max over the 16 * NA accumulator values of a lane. A plain chain: measured
+// faster than a balanced tree here, since the chain can start on the first
+// accumulator while later MFMAs still run.
+template <int NA>
+__device__ inline float max_acc(const f32x16 (&s)[NA]) {
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = fmaxf(m, s[a][r]);
+  return m;
+}
+
+// Combine x of lanes l and l ^ 32 (the two halves of a wave hold the same
+// rows for different columns). v_permlane32_swap runs on the VALU, so the
+// result never waits behind LDS traffic the way a ds_bpermute would; both
+// halves receive the same bits because max and + are commutative.
+__device__ inline float max_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------- block order
+// Workgroups are dispatched to the 8 XCDs round-robin by workgroup index, and
+// each XCD has its own L2. Map grid index t to (head, block) so that every
+// head stays on one XCD (its K/V, or Q/dO, stream is shared in that L2) while
+// block indices still rise with t across all heads: callers put their
+// heaviest blocks at low indices, and those must start first on every XCD,
+// or the longest blocks end up in the tail of the launch. Falls back to
+// head-fastest order when heads don't split evenly over the XCDs. A
+// bijection on [0, heads * per_head) either way.
+__device__ inline void xcd_order(int t, int heads, int per_head, int& head, int& blk) {
+  constexpr int kXcd = 8;
+  if (heads % kXcd == 0) {
+    const int hpx = heads / kXcd;            // heads per XCD
+    const int x = t % kXcd, m = t / kXcd;
+    head = x + kXcd * (m % hpx);
+    blk = m / hpx;
+  } else {
+    head = t % heads;
+    blk = t / heads;
+  }
+}
+
+// ---------------------------------------------------------------- row masks
+// Bit r of the result is set when row q0 + r (0 <= r < 32) lies in [a, b).
+// A key column's masked rows are a union of such intervals, so one word per
+// (key, 32-row window) replaces an interval test per (row, key) element.
+// Any int32 a, b is fine (clamped to the window before subtracting).
+__device__ inline uint32_t row_bits(int a, int b, int q0) {
+  const int lo = min(max(a, q0), q0 + 32) - q0;
+  const int hi = max(min(max(b, q0), q0 + 32) - q0, lo);
+  return (uint32_t)((1ull << hi) - (1ull << lo));
+}
+
+// Masked rows of key column j within the window [q0, q0 + 32): the causal
+// part (rows before j), the lower interval [lts, lte) and the upper interval
+// [uts, ute) (has_ut is false for causal masks). Keys at or past N mask
+// every row.
+__device__ inline uint32_t key_row_mask(int j, int q0, int N, bool causal, bool has_lt,
+                                        bool has_ut, int lts, int lte, int uts, int ute) {
+  uint32_t m = causal ? row_bits(q0, j, q0) : 0u;
+  if (has_lt) m |= row_bits(lts, lte, q0);
+  if (has_ut) m |= row_bits(uts, ute, q0);
+  return j >= N ? ~0u : m;
+}
 
 // ---------------------------------------------------------------- mask rule
 // Per key block: min/max of LTS, LTE, UTS, UTE (8 int32, in that order).

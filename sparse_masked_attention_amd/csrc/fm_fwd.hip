@@ -105,7 +105,7 @@ struct QCfg {
   static constexpr int VEC = 4 * BC * 4;                  // the tile's boundary vectors
   static constexpr int STAGE = 2 * TILE + VEC;
   static constexpr int LIST = 1024;                       // compacted tile list entries
-  static constexpr int LOADS_PER_TILE = 2 * LOADS + 1;    // per wave
+  static constexpr int LOADS_PER_TILE = 2 * LOADS + 1;    // waves 0-3 (they stage a vector)
 };
 
 // XOR swizzle of the 16-byte chunk index within a row: 32 consecutive rows
@@ -130,9 +130,11 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
   // Two pipeline stages as separate LDS objects.
   __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
-  __shared__ int list[C::LIST];
+  __shared__ int list[C::LIST];           // visible key blocks
+  __shared__ unsigned list_cls[C::LIST];  // their per-wave classes, 2 bits each
   __shared__ int wsum[C::NW];
   __shared__ unsigned wcount[3];
+  __shared__ uint32_t mwords[C::NW][C::BC];  // per wave: masked-row word of each key
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -140,8 +142,9 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
   const int hh = lane >> 5;
   const int l32 = lane & 31;
   const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
-  const int qb = p.nqb - 1 - (int)(blockIdx.x / BH);   // heavy (late) query blocks first
+  int bh, qb;
+  xcd_order((int)blockIdx.x, BH, p.nqb, bh, qb);
+  qb = p.nqb - 1 - qb;                                   // heavy (late) query blocks first
   const int b = bh / p.H, h = bh % p.H;
   const int hmi = p.hm == 1 ? 0 : h;
   const int N = p.N;
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
   const long long vrow = ((long long)b * p.hm + hmi) * N;
   const int32_t* vecs[4] = {p.lts, p.lte, p.uts, p.ute};
   // each wave stages one of the four boundary vectors (absent ones read as 0)
-  const int32_t* my_vec = vecs[w];
+  const int32_t* my_vec = vecs[w & 3];
   const bool vec_present = my_vec != nullptr && (w < 2 ? p.has_lt : p.has_ut);
   const __amdgpu_buffer_rsrc_t rvec =
       make_rsrc(vec_present ? my_vec + vrow : p.table, vec_present ? (uint32_t)N * 4 : 0u);
@@ -194,9 +197,9 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
              has_ut = p.has_ut != 0;
 
   // --- issue the loads of one key tile into a stage
-  auto issue = [&](unsigned entry, auto stage_c) {
+  auto issue = [&](int kb, auto stage_c) {
     constexpr int S = decltype(stage_c)::value;
-    const int kbase = (int)(entry & 0xFFFFFFu) * C::BC;
+    const int kbase = kb * C::BC;
     FM_LDS char* st = (FM_LDS char*)(S ? stage1 : stage0);
 #pragma unroll
     for (int u = 0; u < C::LOADS; ++u) {
@@ -206,8 +209,8 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
       load_lds16(rk, st + (w * C::LOADS + u) * 1024, off);
       load_lds16(rv, st + C::TILE + (w * C::LOADS + u) * 1024, off);
     }
-    // 16 lanes x 16 bytes = one 64-key vector per wave
-    if (lane < 16) load_lds16(rvec, st + 2 * C::TILE + w * 256, (uint32_t)(kbase + 4 * lane) * 4);
+    // waves 0-3: 16 lanes x 16 bytes = one 64-key vector each
+    if (w < 4 && lane < 16) load_lds16(rvec, st + 2 * C::TILE + w * 256, (uint32_t)(kbase + 4 * lane) * 4);
   };
 
   // row operand read (32 rows of a tile at one 16-byte chunk)
@@ -227,15 +230,22 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
   };
 
   // --- one key tile of work for this wave
-  auto compute = [&](unsigned entry, auto stage_c) {
+  auto compute = [&](int kb, unsigned cls, auto stage_c) {
     constexpr int S = decltype(stage_c)::value;
-    const int wc = (int)((entry >> (24 + 2 * w)) & 3u);
+    const int wc = (int)((cls >> (2 * w)) & 3u);
     if (wc == 0) return;
-    const int kbase = (int)(entry & 0xFFFFFFu) * C::BC;
+    const int kbase = kb * C::BC;
     const FM_LDS char* kst = (const FM_LDS char*)(S ? stage1 : stage0);
     const FM_LDS char* vst = kst + C::TILE;
     const FM_LDS int* vl = (const FM_LDS int*)(kst + 2 * C::TILE);
     constexpr int JBS = C::JBS;
+    if (wc == 1) {
+      // one key per lane: which of this wave's 32 rows the mask hides for it
+      // (absent vectors were staged as zeros, and has_* gates their use)
+      mwords[w][lane] = key_row_mask(kbase + lane, wr0, N, causal, has_lt, has_ut, vl[lane],
+                                     has_lte ? vl[64 + lane] : N, vl[128 + lane], vl[192 + lane]);
+      __builtin_amdgcn_wave_barrier();
+    }
 #pragma unroll
     for (int hk = 0; hk < C::BC / 32 / JBS; ++hk) {
       // S^T = K Q^T (and dP^T = V dO^T in the dQ pass)
@@ -252,37 +262,22 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
         }
       }
       if (wc == 1) {
-        // element test against the tile's staged bounds
+        // element test: bit l32 (this lane's row) of its key's word
 #pragma unroll
         for (int jj = 0; jj < JBS; ++jj)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int kl = (hk * JBS + jj) * 32 + 8 * g + 4 * hh;
-            const i32x4 lts4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 0 * 64 + kl);
-            const i32x4 lte4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 1 * 64 + kl);
-            // absent vectors were staged as zeros, and has_* gates their use
-            const i32x4 uts4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 2 * 64 + kl);
-            const i32x4 ute4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 3 * 64 + kl);
+            const u32x4 w4 = *(const FM_LDS u32x4*)(FM_LDS uint32_t*)&mwords[w][kl];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int j = kbase + kl + e;
-              const int lte_v = has_lte ? lte4[e] : N;
-              // bitwise (not short-circuit) so this stays a straight-line select
-              const bool m = (j >= N) | (causal & (j > i)) |
-                             (has_lt & (lts4[e] <= i) & (i < lte_v)) |
-                             (has_ut & (uts4[e] <= i) & (i < ute4[e]));
-              s[jj][4 * g + e] = m ? kNegInf : s[jj][4 * g + e];
-            }
+            for (int e = 0; e < 4; ++e)
+              s[jj][4 * g + e] = ((w4[e] >> l32) & 1u) ? kNegInf : s[jj][4 * g + e];
           }
       }
       bf16x8 pf[2 * JBS];
       if constexpr (!DQ) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int jj = 0; jj < JBS; ++jj)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jj][r]);
-        mx = fmaxf(mx, xor32(mx));
+        float mx = max_acc(s);
+        mx = max_x32(mx);
         // move the offset (and rescale O and the sum) only when some row's max
         // outgrew it by more than the slack; a row with nothing open keeps -inf
         if (__ballot((mx - m_run) * p.sl2 > kRescaleSlack) != 0) {
@@ -326,10 +321,11 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
   };
 
   // --- scan the key blocks, compact the visible ones, process in chunks
+  constexpr int NT = C::NW * 64;
   int cnt = 0;
-  for (int base = 0; base < p.nkb; base += 256) {
+  for (int base = 0; base < p.nkb; base += NT) {
     const int kb = base + tid;
-    unsigned entry = 0;
+    unsigned bits = 0;
     bool valid = false;
     if (kb < p.nkb) {
       const BlockBounds bb = load_bounds(table + (long long)kb * 8);
@@ -341,18 +337,16 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
       if (wgc != 0) {
         valid = true;
         const bool ragged = c1 - c0 < C::BC;
-        int bits = 0;
 #pragma unroll
         for (int ww = 0; ww < C::NW; ++ww) {
           const int a0 = r0 + C::WR * ww;
-          int cls = 0;
+          int cl = 0;
           if (a0 < N) {
-            cls = tile_class(bb, a0, min(N, a0 + C::WR), c0, c1, causal);
-            if (ragged && cls == 2) cls = 1;
+            cl = tile_class(bb, a0, min(N, a0 + C::WR), c0, c1, causal);
+            if (ragged && cl == 2) cl = 1;
           }
-          bits |= cls << (2 * ww);
+          bits |= (unsigned)cl << (2 * ww);
         }
-        entry = (unsigned)kb | ((unsigned)bits << 24);
       }
     }
     const unsigned long long bal = __ballot(valid);
@@ -366,25 +360,32 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
       if (ww < w) off += v;
       add += v;
     }
-    if (valid) list[off + rank] = (int)entry;
+    if (valid) {
+      list[off + rank] = kb;
+      list_cls[off + rank] = bits;
+    }
     __syncthreads();
     cnt += add;
-    if (cnt > C::LIST - 256 || base + 256 >= p.nkb) {
+    if (cnt > C::LIST - NT || base + NT >= p.nkb) {
       // process the compacted list with a two-stage load pipeline
       auto step = [&](int it, auto stage_c) {
         constexpr int S = decltype(stage_c)::value;
-        const unsigned entry_it = (unsigned)list[it];
+        // uniform across the wave: keeps the class tests scalar branches
+        const int kb_it = uniform(list[it]);
+        const unsigned cls_it = uniform_u32(list_cls[it]);
         if (it + 1 < cnt) {
-          issue((unsigned)list[it + 1], std::integral_constant<int, 1 - S>{});
-          wait_vmcnt<C::LOADS_PER_TILE>();
+          issue(list[it + 1], std::integral_constant<int, 1 - S>{});
+          // waves 0-3 issued one more load (a boundary vector)
+          if (w < 4) wait_vmcnt<C::LOADS_PER_TILE>();
+          else wait_vmcnt<C::LOADS_PER_TILE - 1>();
         } else {
           wait_vmcnt<0>();
         }
         lds_barrier();
-        compute(entry_it, stage_c);
+        compute(kb_it, cls_it, stage_c);
         lds_barrier();
       };
-      if (cnt > 0) issue((unsigned)list[0], std::integral_constant<int, 0>{});
+      if (cnt > 0) issue(list[0], std::integral_constant<int, 0>{});
       for (int it = 0; it < cnt; it += 2) {
         step(it, std::integral_constant<int, 0>{});
         if (it + 1 < cnt) step(it + 1, std::integral_constant<int, 1>{});
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
   // --- epilogue
   if constexpr (!DQ) {
     // normalise, store O (bf16) and the natural-log LSE
-    const float lt = l_run + xor32(l_run);
+    const float lt = sum_x32(l_run);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (i < N) {
       bf16* og = reinterpret_cast<bf16*>(p.o) + (slice + i) * D;
@@ -514,12 +515,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) mask_block(s[jb], (const FM_LDS int*)vl, jb * 32, c0, i, p, hh);
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
-    mx = fmaxf(mx, xor32(mx));
+    float mx = max_acc(s);
+    mx = max_x32(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = exp2f((m_run - m_use) * p.sl2);
@@ -547,7 +544,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
         }
   }
 
-  const float lt = l_run + xor32(l_run);
+  const float lt = sum_x32(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (i < N) {
     float* og = reinterpret_cast<float*>(p.o) + (slice + i) * D;
@@ -575,7 +572,7 @@ static hipError_t launch_qmajor(FwdParams p, hipStream_t stream) {
   using C = QCfg<D, MODE>;
   p.nqb = (p.N + C::BR - 1) / C::BR;
   const long long grid = (long long)p.B * p.H * p.nqb;
-  hipLaunchKernelGGL((qmajor_bf16_kernel<D, MODE>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((qmajor_bf16_kernel<D, MODE>), dim3((unsigned)grid), dim3(C::NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ constexpr int kTableBlock = 64;
 
 // Tile shapes the attention kernels classify (query rows x key columns).
 constexpr int kFwdBlockK = 64;
-// forward query-block height (4 waves x 32 rows)
+// forward query-block height: 4 waves x 32 rows for every head dim and dtype
 inline int fwd_block_q(int d, int is_bf16) { (void)d; (void)is_bf16; return 128; }
 constexpr int kBwdBlockK = 128;
 // backward query-block height: 64 rows for bf16 with d <= 128, else 32
