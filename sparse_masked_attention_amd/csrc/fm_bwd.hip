@@ -57,9 +57,10 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------- preprocess
-// delta_i = sum_m dO[i][m] * O[i][m] in float32; LSE in base-2 units (+inf
-// where the row is fully masked, so exp2(s - LSE2) is 0 there); for the fp32
-// path also zero the dQ accumulator rows. 16 threads per row, 16-byte chunks.
+// fp32 path: delta_i = sum_m dO[i][m] * O[i][m] in float32; LSE in base-2
+// units (+inf where the row is fully masked, so exp2(s - LSE2) is 0 there);
+// zero the dQ accumulator rows. 16 threads per row, 16-byte chunks. (The
+// bf16 path computes delta and the base-2 LSE inside its dQ pass.)
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   const long long rows = (long long)p.B * p.H * p.N;
@@ -251,56 +252,58 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const FM_LDS float* del_l = lse_l + C::BQ;
     const int q0 = (int)(entry & 0xFFFFFFu) * C::BQ;
     bf16x8 pB[C::BQ / 16], dsB[C::BQ / 16];
-    {
-      f32x16 sacc[C::BQ / 32], dpacc[C::BQ / 32];
+    constexpr int NIB = C::BQ / 32;          // 32-row halves of the tile
+    // The S accumulators start at the mask's additive bias (-inf where the
+    // element is masked, else 0), so the MFMAs apply the mask and the code
+    // below is the same for every tile class.
+    f32x16 sacc[NIB], dpacc[NIB];
+    if (wc == 1) {
 #pragma unroll
-      for (int ib = 0; ib < C::BQ / 32; ++ib) {
-        sacc[ib] = f32x16{};
-        dpacc[ib] = f32x16{};
-        const int row = 32 * ib + l32;
+      for (int ib = 0; ib < NIB; ++ib) {
+        // masked rows of this lane's key among rows q0 + 32 ib + [0, 32)
+        // (rows past N too: their staged LSE is not +inf), shifted so that
+        // bit 8 g + e is the row of register 4 g + e
+        const int rb = q0 + 32 * ib;
+        const uint32_t mw = (key_row_mask(j, rb, N, causal, has_lt, has_ut, k_lts, k_lte, k_uts, k_ute) |
+                             row_bits(N, rb + 32, rb)) >> (4 * hh);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          sacc[ib] = mfma32(lds_read_b128(tile_addr<D>(qst, row, 16 * c + 8 * hh)), kB[c], sacc[ib]);
-          dpacc[ib] = mfma32(lds_read_b128(tile_addr<D>(dost, row, 16 * c + 8 * hh)), vB[c], dpacc[ib]);
-        }
+        for (int r = 0; r < 16; ++r) sacc[ib][r] = ((mw >> (8 * (r / 4) + r % 4)) & 1u) ? kNegInf : 0.f;
       }
-      if (wc == 1) {
+    } else {
 #pragma unroll
-        for (int ib = 0; ib < C::BQ / 32; ++ib) {
-          // masked rows of this lane's key among rows q0 + 32 ib + [0, 32)
-          // (rows past N too: their staged LSE is not +inf), shifted so that
-          // bit 8 g + e is the row of register 4 g + e
-          const int rb = q0 + 32 * ib;
-          const uint32_t mw = (key_row_mask(j, rb, N, causal, has_lt, has_ut, k_lts, k_lte, k_uts, k_ute) |
-                               row_bits(N, rb + 32, rb)) >> (4 * hh);
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sacc[ib][r] = ((mw >> (8 * (r / 4) + r % 4)) & 1u) ? kNegInf : sacc[ib][r];
-        }
-      }
-#pragma unroll
-      for (int ib = 0; ib < C::BQ / 32; ++ib) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int rl = 32 * ib + 8 * g + 4 * hh;   // first of 4 rows held
-          const f32x4 lse4 = *reinterpret_cast<const FM_LDS f32x4*>(lse_l + rl);
-          const f32x4 del4 = *reinterpret_cast<const FM_LDS f32x4*>(del_l + rl);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            const float s = sacc[ib][r];
-            // P = exp2(S * scale * log2e - LSE2); fully masked rows have LSE2 = +inf
-            const float pv = fast_exp2(__builtin_fmaf(s, p.sl2, -lse4[e]));
-            pB[2 * ib + r / 8][r % 8] = (bf16)pv;
-            dsB[2 * ib + r / 8][r % 8] = (bf16)(pv * (dpacc[ib][r] - del4[e]));
-          }
-        }
-      }
+      for (int ib = 0; ib < NIB; ++ib) sacc[ib] = f32x16{};
     }
-    // dV += P^T dO and dK += dS^T Q; dO / Q operands by transposed reads
-    const int sl = lane & 15;
+    // S = Q K^T + bias and dP = dO V^T for rows 32 ib .. 32 ib + 31
+    auto sdp = [&](int ib) {
+      dpacc[ib] = f32x16{};
+      const int row = 32 * ib + l32;
 #pragma unroll
-    for (int c = 0; c < C::BQ / 16; ++c) {
+      for (int c = 0; c < D / 16; ++c) {
+        sacc[ib] = mfma32(lds_read_b128(tile_addr<D>(qst, row, 16 * c + 8 * hh)), kB[c], sacc[ib]);
+        dpacc[ib] = mfma32(lds_read_b128(tile_addr<D>(dost, row, 16 * c + 8 * hh)), vB[c], dpacc[ib]);
+      }
+    };
+    // P = exp2(S * scale * log2e - LSE2) and dS = P (dP - delta), as bf16
+    // B operands; fully masked rows have LSE2 = +inf
+    auto probs = [&](int ib) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int rl = 32 * ib + 8 * g + 4 * hh;   // first of 4 rows held
+        const f32x4 lse4 = *reinterpret_cast<const FM_LDS f32x4*>(lse_l + rl);
+        const f32x4 del4 = *reinterpret_cast<const FM_LDS f32x4*>(del_l + rl);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float pv = fast_exp2(__builtin_fmaf(sacc[ib][r], p.sl2, -lse4[e]));
+          pB[2 * ib + r / 8][r % 8] = (bf16)pv;
+          dsB[2 * ib + r / 8][r % 8] = (bf16)(pv * (dpacc[ib][r] - del4[e]));
+        }
+      }
+    };
+    // dV += P^T dO and dK += dS^T Q over the 16 rows of chunk c; dO / Q
+    // operands by transposed reads
+    const int sl = lane & 15;
+    auto dvdk = [&](int c) {
       const int ra = 16 * c + 4 * hh + (sl >> 2);
       const int rb = ra + 8;
 #pragma unroll
@@ -311,6 +314,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         const bf16x8 bq = cat(lds_read_tr(tile_addr<D>(qst, ra, col)), lds_read_tr(tile_addr<D>(qst, rb, col)));
         dkacc[mb] = mfma32(dsB[c], bq, dkacc[mb]);
       }
+    };
+    // Software-pipelined over the two row halves, so the exponentials of
+    // one half run on the VALU while the MFMAs of the other run; the
+    // scheduling fences keep the compiler from regrouping the phases.
+    sdp(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NIB == 2) {
+      sdp(1);
+      probs(0);
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk(0);
+      dvdk(1);
+      probs(1);
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk(2);
+      dvdk(3);
+    } else {
+      probs(0);
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk(0);
+      dvdk(1);
     }
   };
 
@@ -613,9 +637,8 @@ static hipError_t launch_convert(const BwdParams& p, int d, hipStream_t stream) 
 template <int D>
 static hipError_t launch_bwd_bf16(BwdParams p, const AttnArgs& a, hipStream_t stream) {
   p.nqb = (p.N + BwdCfg<D>::BQ - 1) / BwdCfg<D>::BQ;
-  hipError_t e = launch_pre<D, bf16>(p, stream);
-  if (e != hipSuccess) return e;
-  e = launch_bwd_dq(a, p.lse2, stream);
+  // the dQ pass also writes delta and the base-2 LSE the dK/dV pass reads
+  const hipError_t e = launch_bwd_dq(a, stream);
   if (e != hipSuccess) return e;
   const long long grid = (long long)p.B * p.H * p.nkb * BwdCfg<D>::NSPLIT;
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);

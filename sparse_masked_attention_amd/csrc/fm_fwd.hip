@@ -40,10 +40,14 @@ struct FwdParams {
   void* o;
   float* lse;
   unsigned long long* counts;
-  // dQ mode (backward): dO, the base-2 logsumexp and delta per row, dQ out
+  // dQ mode (backward): dO and the forward's O and natural-log LSE in; dQ
+  // out, and per row the base-2 LSE and delta = rowsum(dO * O) out for the
+  // dK/dV pass
   const void* dout;
-  const float* lse2;
-  const float* delta;
+  const void* o_in;
+  const float* lse_in;
+  float* lse2;
+  float* delta;
   void* dq;
   int B, H, N, hm, causal;
   int has_lt, has_lte, has_ut;
@@ -180,9 +184,26 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
       dof[c] = __builtin_bit_cast(bf16x8, buffer_load16(rdo, (uint32_t)(i * D + 16 * c + 8 * hh) * 2));
-    // fully masked rows carry +inf here, so their P is 0
-    row_lse2 = i < N ? p.lse2[slice + i] : __builtin_inff();
-    row_delta = i < N ? p.delta[slice + i] : 0.f;
+    // delta_i = dO_i . O_i: this lane holds half of row i (the chunks of
+    // its half-wave), the other half-wave the rest
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<const bf16*>(p.o_in) + slice * D, tbytes);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    float dl = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const bf16x8 oc = __builtin_bit_cast(bf16x8, buffer_load16(ro, (uint32_t)(i * D + 16 * c + 8 * hh) * 2));
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        dl = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{dof[c][e], dof[c][e + 1]}, bf16x2_t{oc[e], oc[e + 1]}, dl, false);
+    }
+    row_delta = sum_x32(dl);
+    // base-2 LSE; a fully masked row (LSE -inf) gets +inf, so its P is 0
+    const float l = i < N ? p.lse_in[slice + i] : kNegInf;
+    row_lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+    if (hh == 0 && i < N) {
+      p.delta[slice + i] = row_delta;
+      p.lse2[slice + i] = row_lse2;
+    }
   }
 
   f32x16 oacc[D / 32];           // O^T (forward) or dQ^T (dQ pass)
@@ -246,77 +267,96 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
                                      has_lte ? vl[64 + lane] : N, vl[128 + lane], vl[192 + lane]);
       __builtin_amdgcn_wave_barrier();
     }
+    // S^T starts at the mask's additive bias (-inf where masked, else 0): the
+    // MFMAs apply the mask, and the code after them is the same for every
+    // tile class. Element test: bit l32 (this lane's row) of the word of
+    // the element's key.
+    auto bias = [&](f32x16& sx, int kb32) {
+      if (wc == 1) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int kl = kb32 * 32 + 8 * g + 4 * hh;
+          const u32x4 w4 = *(const FM_LDS u32x4*)(FM_LDS uint32_t*)&mwords[w][kl];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sx[4 * g + e] = ((w4[e] >> l32) & 1u) ? kNegInf : 0.f;
+        }
+      } else {
+        sx = f32x16{};
+      }
+    };
+    if constexpr (DQ) {
+      // dQ pass, one 32-key half at a time (two workgroups per CU hide the
+      // latencies; holding both halves at once would need one per CU)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        f32x16 s, dp = f32x16{};
+        bias(s, jb);
+        const int row = jb * 32 + l32;
+        // S^T = K Q^T + bias, dP^T = V dO^T
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          s = mfma32(row_read(kst, row, 2 * c + hh), qf[c], s);
+          dp = mfma32(row_read(vst, row, 2 * c + hh), dof[c], dp);
+        }
+        // dS = P (dP - delta) with P = exp2(S * scale * log2e - LSE2)
+        bf16x8 pf[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = fast_exp2(__builtin_fmaf(s[r], p.sl2, -row_lse2));
+          pf[r / 8][r % 8] = (bf16)(pv * (dp[r] - row_delta));
+        }
+        // dQ^T += K^T dS^T over the half's keys
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32(tr_read(kst, 2 * jb + cc, mb), pf[cc], oacc[mb]);
+      }
+    } else {
 #pragma unroll
     for (int hk = 0; hk < C::BC / 32 / JBS; ++hk) {
-      // S^T = K Q^T (and dP^T = V dO^T in the dQ pass)
-      f32x16 s[JBS], dp[DQ ? JBS : 1];
+      f32x16 s[JBS];
+#pragma unroll
+      for (int jj = 0; jj < JBS; ++jj) bias(s[jj], hk * JBS + jj);
+      // S^T = K Q^T
 #pragma unroll
       for (int jj = 0; jj < JBS; ++jj) {
         const int row = (hk * JBS + jj) * 32 + l32;
-        s[jj] = f32x16{};
-        if constexpr (DQ) dp[jj] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          s[jj] = mfma32(row_read(kst, row, 2 * c + hh), qf[c], s[jj]);
-          if constexpr (DQ) dp[jj] = mfma32(row_read(vst, row, 2 * c + hh), dof[c], dp[jj]);
-        }
-      }
-      if (wc == 1) {
-        // element test: bit l32 (this lane's row) of its key's word
-#pragma unroll
-        for (int jj = 0; jj < JBS; ++jj)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int kl = (hk * JBS + jj) * 32 + 8 * g + 4 * hh;
-            const u32x4 w4 = *(const FM_LDS u32x4*)(FM_LDS uint32_t*)&mwords[w][kl];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              s[jj][4 * g + e] = ((w4[e] >> l32) & 1u) ? kNegInf : s[jj][4 * g + e];
-          }
+        for (int c = 0; c < D / 16; ++c) s[jj] = mfma32(row_read(kst, row, 2 * c + hh), qf[c], s[jj]);
       }
       bf16x8 pf[2 * JBS];
-      if constexpr (!DQ) {
-        float mx = max_acc(s);
-        mx = max_x32(mx);
-        // move the offset (and rescale O and the sum) only when some row's max
-        // outgrew it by more than the slack; a row with nothing open keeps -inf
-        if (__ballot((mx - m_run) * p.sl2 > kRescaleSlack) != 0) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = m_new == kNegInf ? 1.f : fast_exp2((m_run - m_new) * p.sl2);
-          l_run *= alpha;
+      float mx = max_acc(s);
+      mx = max_x32(mx);
+      // move the offset (and rescale O and the sum) only when some row's max
+      // outgrew it by more than the slack; a row with nothing open keeps -inf
+      if (__ballot((mx - m_run) * p.sl2 > kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == kNegInf ? 1.f : fast_exp2((m_run - m_new) * p.sl2);
+        l_run *= alpha;
 #pragma unroll
-          for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
-          m_run = m_new;
-        }
-        const float msl = (m_run == kNegInf ? 0.f : m_run) * p.sl2;
-#pragma unroll
-        for (int jj = 0; jj < JBS; ++jj)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            pf[2 * jj + r / 8][r % 8] = (bf16)fast_exp2(__builtin_fmaf(s[jj][r], p.sl2, -msl));
-        // row sum of the rounded probabilities (the values the PV MFMA
-        // uses), two per v_dot2_f32_bf16
-        float rs = l_run;
-#pragma unroll
-        for (int c = 0; c < 2 * JBS; ++c) rs = sum8_bf16(pf[c], rs);
-        l_run = rs;
-      } else {
-        // dS = P * (dP - delta) with P = exp2(S * scale * log2e - LSE2)
-#pragma unroll
-        for (int jj = 0; jj < JBS; ++jj)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pv = fast_exp2(__builtin_fmaf(s[jj][r], p.sl2, -row_lse2));
-            pf[2 * jj + r / 8][r % 8] = (bf16)(pv * (dp[jj][r] - row_delta));
-          }
+        for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+        m_run = m_new;
       }
-      // O^T += V^T P^T (forward) or dQ^T += K^T dS^T (dQ pass)
+      const float msl = (m_run == kNegInf ? 0.f : m_run) * p.sl2;
+#pragma unroll
+      for (int jj = 0; jj < JBS; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          pf[2 * jj + r / 8][r % 8] = (bf16)fast_exp2(__builtin_fmaf(s[jj][r], p.sl2, -msl));
+      // row sum of the rounded probabilities (the values the PV MFMA
+      // uses), two per v_dot2_f32_bf16
+      float rs = l_run;
+#pragma unroll
+      for (int c = 0; c < 2 * JBS; ++c) rs = sum8_bf16(pf[c], rs);
+      l_run = rs;
+      // O^T += V^T P^T
 #pragma unroll
       for (int cc = 0; cc < 2 * JBS; ++cc) {
         const int c = 2 * JBS * hk + cc;
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32(tr_read(DQ ? kst : vst, c, mb), pf[cc], oacc[mb]);
+        for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32(tr_read(vst, c, mb), pf[cc], oacc[mb]);
       }
+    }
     }
   };
 
@@ -628,7 +668,7 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
 namespace fm {
 
 // dQ pass of the backward (query-major; see qmajor_bf16_kernel).
-hipError_t launch_bwd_dq(const AttnArgs& a, const float* lse2, hipStream_t stream) {
+hipError_t launch_bwd_dq(const AttnArgs& a, hipStream_t stream) {
   FwdParams p{};
   p.q = a.q;
   p.k = a.k;
@@ -639,7 +679,9 @@ hipError_t launch_bwd_dq(const AttnArgs& a, const float* lse2, hipStream_t strea
   p.ute = a.mask.ute;
   p.table = a.table;
   p.dout = a.dout;
-  p.lse2 = lse2;
+  p.o_in = a.o;
+  p.lse_in = a.lse;
+  p.lse2 = a.lse2;
   p.delta = a.delta;
   p.dq = a.dq;
   p.B = a.B;

@@ -56,6 +56,6 @@ hipError_t launch_classify(const int32_t* table, int B, int hm, int N, int causa
                            int block_k, int8_t* out, hipStream_t stream);
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_bwd_dq(const AttnArgs& a, const float* lse2, hipStream_t stream);
+hipError_t launch_bwd_dq(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace fm
