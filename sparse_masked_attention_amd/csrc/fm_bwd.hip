@@ -353,6 +353,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
     kbnd = m;
   }
+  // K, V, the key bounds and the table entries are all needed before the
+  // first tile. Waiting for them here (the scan needs the table anyway) also
+  // tells the compiler nothing of its own is in flight inside the tile loop,
+  // where its waits would otherwise stall on the tile prefetch as well.
+  wait_vmcnt<0>();
   int cnt = 0;
   for (int base = 0; base < p.nqb; base += 256) {
     const int qb = base + tid;
