@@ -37,8 +37,10 @@
  *     library keeps no mutable global state.
  *   - B * H * N == 0 is a successful no-op. Offsets are 64-bit.
  *   - softmax_scale <= 0 or NaN selects 1/sqrt(d).
- *   - Supported: dtype FM_BF16 with d == dv in {64, 128, 256}; FM_FP32 with
- *     d == dv in {64, 128} (forward and backward). Others: FM_ERROR_NOT_SUPPORTED.
+ *   - Supported (forward and backward): dtype FM_BF16 with d == dv in
+ *     {64, 128, 256} or d = 192 with dv = 128 (Q/K head dim larger than V's,
+ *     README "News": large head dims); FM_FP32 with d == dv in {64, 128}.
+ *     Others: FM_ERROR_NOT_SUPPORTED.
  */
 #ifndef FLASHMASK_H
 #define FLASHMASK_H

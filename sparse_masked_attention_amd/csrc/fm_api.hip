@@ -16,15 +16,20 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
+// bf16: d = dv in {64, 128, 256} and (d, dv) = (192, 128); fp32: d = dv in
+// {64, 128}. Forward and backward cover the same set.
 bool supported(int d, int dv, fm_dtype_t dtype) {
-  if (d != dv) return false;
-  if (dtype == FM_BF16) return d == 64 || d == 128 || d == 256;
-  if (dtype == FM_FP32) return d == 64 || d == 128;
+  if (dtype == FM_BF16) return fm::bf16_dims(d, dv);
+  if (dtype == FM_FP32) return fm::fp32_dims(d, dv);
   return false;
 }
 
-// Backward kernels: bf16 with d = dv in {64, 128, 256}, fp32 with {64, 128}.
 bool bwd_supported(int d, int dv, fm_dtype_t dtype) { return supported(d, dv, dtype); }
+
+// some dv makes (d, dv) supported: the tile shape depends on d only
+bool supported_d(int d, fm_dtype_t dtype) {
+  return supported(d, d, dtype) || (dtype == FM_BF16 && fm::bf16_dims(d, 128));
+}
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -86,7 +91,7 @@ int flashmask_table_block(void) { return kTableBlock; }
 
 fm_status_t flashmask_tile_shape(int is_bwd, int d, fm_dtype_t dtype, int* block_q, int* block_k) {
   if (block_q == nullptr || block_k == nullptr) return FM_ERROR_INVALID_VALUE;
-  if (!supported(d, d, dtype)) return FM_ERROR_NOT_SUPPORTED;
+  if (!supported_d(d, dtype)) return FM_ERROR_NOT_SUPPORTED;
   *block_q = is_bwd ? fm::bwd_block_q(d, dtype == FM_BF16) : fm::fwd_block_q(d, dtype == FM_BF16);
   *block_k = is_bwd ? fm::kBwdBlockK : fm::kFwdBlockK;
   return FM_SUCCESS;

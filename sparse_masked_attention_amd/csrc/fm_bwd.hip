@@ -126,27 +126,34 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 // d = 256 does not fit dK and dV of 32 keys per wave in registers; it runs as
 // two workgroups per key block, each owning half of the dK/dV columns and
 // recomputing S and dP in full.
-template <int D>
+// D: head dim of Q and K (and dQ, dK); DV: head dim of V (and dO, dV).
+template <int D, int DV>
 struct BwdCfg {
   static constexpr int NW = 4;
   static constexpr int KW = 32;                 // keys per wave
   static constexpr int BKC = NW * KW;           // keys per workgroup
-  static constexpr int NSPLIT = D > 128 ? 2 : 1;
-  static constexpr int DO = D / NSPLIT;         // output columns per workgroup
+  static constexpr int NSPLIT = D >= 256 ? 2 : 1;
+  static constexpr int DO = D / NSPLIT;         // dK columns per workgroup
+  static constexpr int DVO = DV / NSPLIT;       // dV columns per workgroup
   static constexpr int BQ = D > 128 ? 32 : 64;  // query rows per step
-  static constexpr int CH = D / 8;
-  static constexpr int QT = BQ * D * 2;         // bytes of one Q or dO tile
-  static constexpr int LOADS = QT / (NW * 1024);
-  static constexpr int STAGE = 2 * QT + 2 * BQ * 4;  // Q, dO, LSE2, delta
+  static constexpr int CHQ = D / 8;             // 16-byte chunks per Q row
+  static constexpr int CHO = DV / 8;            // 16-byte chunks per dO row
+  static constexpr int QT = BQ * D * 2;         // bytes of one Q tile
+  static constexpr int OT = BQ * DV * 2;        // bytes of one dO tile
+  static constexpr int LOADS_Q = QT / (NW * 1024);
+  static constexpr int LOADS_O = OT / (NW * 1024);
+  static constexpr int STAGE = QT + OT + 2 * BQ * 4;  // Q, dO, LSE2, delta
   static constexpr int LIST = 1024;
-  static constexpr int LOADS_PER_STEP = 2 * LOADS + 1;   // waves 0/1 add LSE2 / delta
+  static constexpr int LOADS_PER_STEP = LOADS_Q + LOADS_O + 1;   // waves 0/1 add LSE2 / delta
 };
 
 // Chunk swizzle shared by row reads (32 rows, one chunk) and transposed reads
 // (8 rows x 4 chunks) of the Q and dO tiles.
 template <int W>
 __device__ inline int swz(int row) {
-  if constexpr (W >= 128) return 4 * (row & 3) + ((row >> 2) & 3);
+  static_assert(W == 64 || W == 128 || W == 192 || W == 256, "row width");
+  if constexpr (W == 192) return (row >> 1) & 7;   // 24 chunks: stay inside each group of 8
+  else if constexpr (W >= 128) return 4 * (row & 3) + ((row >> 2) & 3);
   else return 4 * (row & 1) + ((row >> 1) & 3);
 }
 
@@ -156,9 +163,9 @@ __device__ inline const FM_LDS char* tile_addr(const FM_LDS char* base, int row,
   return base + row * W * 2 + (((col >> 3) ^ swz<W>(row)) << 4) + (col & 7) * 2;
 }
 
-template <int D>
+template <int D, int DV>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  using C = BwdCfg<D>;
+  using C = BwdCfg<D, DV>;
   __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
   __shared__ int list[C::LIST];
@@ -175,7 +182,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   xcd_order((int)blockIdx.x, BH, p.nkb * C::NSPLIT, bh, rest);
   const int kb = rest / C::NSPLIT;
   const int sp = rest % C::NSPLIT;           // which output column half
-  const int col0 = sp * C::DO;
+  const int col0 = sp * C::DO;               // first dK column of this workgroup
+  const int col0v = sp * C::DVO;             // first dV column
   const int b = bh / p.H, h = bh % p.H;
   const int hmi = p.hm == 1 ? 0 : h;
   const int N = p.N;
@@ -184,22 +192,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int c1 = min(N, c0 + C::BKC);
   const int wc0 = c0 + C::KW * w;                // this wave's first key
   const int j = wc0 + l32;                        // this lane's key
-  const uint32_t tbytes = (uint32_t)N * D * 2;
+  const uint32_t tbytes = (uint32_t)N * D * 2;     // one head of Q or K
+  const uint32_t vbytes = (uint32_t)N * DV * 2;    // one head of V or dO
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(p.q) + slice * D, tbytes);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + slice * D, tbytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + slice * D, tbytes);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const bf16*>(p.dout) + slice * D, tbytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + slice * DV, vbytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const bf16*>(p.dout) + slice * DV, vbytes);
   const __amdgpu_buffer_rsrc_t rlse = make_rsrc(p.lse2 + slice, (uint32_t)N * 4);
   const __amdgpu_buffer_rsrc_t rdel = make_rsrc(p.delta + slice, (uint32_t)N * 4);
 
   // K and V of this lane's key as the B operands of S = Q K^T and dP = dO V^T
-  bf16x8 kB[D / 16], vB[D / 16];
+  bf16x8 kB[D / 16], vB[DV / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
+  for (int c = 0; c < D / 16; ++c)
     kB[c] = __builtin_bit_cast(bf16x8, buffer_load16(rk, (uint32_t)(j * D + 16 * c + 8 * hh) * 2));
-    vB[c] = __builtin_bit_cast(bf16x8, buffer_load16(rv, (uint32_t)(j * D + 16 * c + 8 * hh) * 2));
-  }
+#pragma unroll
+  for (int c = 0; c < DV / 16; ++c)
+    vB[c] = __builtin_bit_cast(bf16x8, buffer_load16(rv, (uint32_t)(j * DV + 16 * c + 8 * hh) * 2));
   // this lane's key bounds (the element test needs nothing else)
   const long long vrow = ((long long)b * p.hm + hmi) * N;
   int k_lts = N, k_lte = N, k_uts = 0, k_ute = 0;
@@ -215,12 +225,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   }
   const bool causal = p.causal != 0, has_lt = p.has_lt != 0, has_ut = p.has_ut != 0;
 
-  f32x16 dvacc[C::DO / 32], dkacc[C::DO / 32];
+  f32x16 dvacc[C::DVO / 32], dkacc[C::DO / 32];
 #pragma unroll
-  for (int mb = 0; mb < C::DO / 32; ++mb) {
-    dvacc[mb] = f32x16{};
-    dkacc[mb] = f32x16{};
-  }
+  for (int mb = 0; mb < C::DVO / 32; ++mb) dvacc[mb] = f32x16{};
+#pragma unroll
+  for (int mb = 0; mb < C::DO / 32; ++mb) dkacc[mb] = f32x16{};
   if (tid < 3) wcount[tid] = 0;
   unsigned cnt0 = 0, cnt1 = 0, cnt2 = 0;
   const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb64 * 8;
@@ -230,16 +239,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     FM_LDS char* st = (FM_LDS char*)(S ? stage1 : stage0);
     const int q0 = (int)(entry & 0xFFFFFFu) * C::BQ;
 #pragma unroll
-    for (int u = 0; u < C::LOADS; ++u) {
-      const int g = (w * C::LOADS + u) * 64 + lane;
-      const int row = g / C::CH, pch = g % C::CH;
-      const uint32_t off = (uint32_t)((q0 + row) * D + 8 * (pch ^ swz<D>(row))) * 2;
-      load_lds16(rq, st + (w * C::LOADS + u) * 1024, off);
-      load_lds16(rdo, st + C::QT + (w * C::LOADS + u) * 1024, off);
+    for (int u = 0; u < C::LOADS_Q; ++u) {
+      const int g = (w * C::LOADS_Q + u) * 64 + lane;
+      const int row = g / C::CHQ, pch = g % C::CHQ;
+      load_lds16(rq, st + (w * C::LOADS_Q + u) * 1024,
+                 (uint32_t)((q0 + row) * D + 8 * (pch ^ swz<D>(row))) * 2);
+    }
+#pragma unroll
+    for (int u = 0; u < C::LOADS_O; ++u) {
+      const int g = (w * C::LOADS_O + u) * 64 + lane;
+      const int row = g / C::CHO, pch = g % C::CHO;
+      load_lds16(rdo, st + C::QT + (w * C::LOADS_O + u) * 1024,
+                 (uint32_t)((q0 + row) * DV + 8 * (pch ^ swz<DV>(row))) * 2);
     }
     // BQ base-2 LSE values then BQ delta values, 16 bytes per lane
     if (w < 2 && lane < C::BQ / 4)
-      load_lds16(w == 0 ? rlse : rdel, st + 2 * C::QT + w * C::BQ * 4, (uint32_t)(q0 + 4 * lane) * 4);
+      load_lds16(w == 0 ? rlse : rdel, st + C::QT + C::OT + w * C::BQ * 4, (uint32_t)(q0 + 4 * lane) * 4);
   };
 
   auto compute = [&](unsigned entry, auto stage_c) {
@@ -248,7 +263,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     if (wc == 0) return;
     const FM_LDS char* qst = (const FM_LDS char*)(S ? stage1 : stage0);
     const FM_LDS char* dost = qst + C::QT;
-    const FM_LDS float* lse_l = (const FM_LDS float*)(qst + 2 * C::QT);
+    const FM_LDS float* lse_l = (const FM_LDS float*)(qst + C::QT + C::OT);
     const FM_LDS float* del_l = lse_l + C::BQ;
     const int q0 = (int)(entry & 0xFFFFFFu) * C::BQ;
     bf16x8 pB[C::BQ / 16], dsB[C::BQ / 16];
@@ -278,10 +293,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       dpacc[ib] = f32x16{};
       const int row = 32 * ib + l32;
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
+      for (int c = 0; c < D / 16; ++c)
         sacc[ib] = mfma32(lds_read_b128(tile_addr<D>(qst, row, 16 * c + 8 * hh)), kB[c], sacc[ib]);
-        dpacc[ib] = mfma32(lds_read_b128(tile_addr<D>(dost, row, 16 * c + 8 * hh)), vB[c], dpacc[ib]);
-      }
+#pragma unroll
+      for (int c = 0; c < DV / 16; ++c)
+        dpacc[ib] = mfma32(lds_read_b128(tile_addr<DV>(dost, row, 16 * c + 8 * hh)), vB[c], dpacc[ib]);
     };
     // P = exp2(S * scale * log2e - LSE2) and dS = P (dP - delta), as bf16
     // B operands; fully masked rows have LSE2 = +inf
@@ -306,11 +322,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     auto dvdk = [&](int c) {
       const int ra = 16 * c + 4 * hh + (sl >> 2);
       const int rb = ra + 8;
+      const int cl = 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+#pragma unroll
+      for (int mb = 0; mb < C::DVO / 32; ++mb) {
+        const int col = col0v + 32 * mb + cl;
+        const bf16x8 bo = cat(lds_read_tr(tile_addr<DV>(dost, ra, col)), lds_read_tr(tile_addr<DV>(dost, rb, col)));
+        dvacc[mb] = mfma32(pB[c], bo, dvacc[mb]);
+      }
 #pragma unroll
       for (int mb = 0; mb < C::DO / 32; ++mb) {
-        const int col = col0 + 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
-        const bf16x8 bo = cat(lds_read_tr(tile_addr<D>(dost, ra, col)), lds_read_tr(tile_addr<D>(dost, rb, col)));
-        dvacc[mb] = mfma32(pB[c], bo, dvacc[mb]);
+        const int col = col0 + 32 * mb + cl;
         const bf16x8 bq = cat(lds_read_tr(tile_addr<D>(qst, ra, col)), lds_read_tr(tile_addr<D>(qst, rb, col)));
         dkacc[mb] = mfma32(dsB[c], bq, dkacc[mb]);
       }
@@ -431,17 +452,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   // --- write dK = scale * dS^T Q and dV for this wave's keys
   if (wc0 < N) {
     bf16* dkg = reinterpret_cast<bf16*>(p.dk) + slice * D;
-    bf16* dvg = reinterpret_cast<bf16*>(p.dv) + slice * D;
+    bf16* dvg = reinterpret_cast<bf16*>(p.dv) + slice * DV;
 #pragma unroll
-    for (int mb = 0; mb < C::DO / 32; ++mb)
+    for (int r = 0; r < 16; ++r) {
+      const int key = wc0 + 8 * (r / 4) + 4 * hh + (r % 4);
+      if (key < N) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = wc0 + 8 * (r / 4) + 4 * hh + (r % 4);
-        if (key < N) {
+        for (int mb = 0; mb < C::DO / 32; ++mb)
           dkg[(long long)key * D + col0 + 32 * mb + l32] = (bf16)(dkacc[mb][r] * p.scale);
-          dvg[(long long)key * D + col0 + 32 * mb + l32] = (bf16)dvacc[mb][r];
-        }
+#pragma unroll
+        for (int mb = 0; mb < C::DVO / 32; ++mb)
+          dvg[(long long)key * DV + col0v + 32 * mb + l32] = (bf16)dvacc[mb][r];
       }
+    }
   }
   if (p.counts != nullptr && sp == 0) {
     atomicAdd(&wcount[0], cnt0);
@@ -639,14 +662,15 @@ static hipError_t launch_convert(const BwdParams& p, int d, hipStream_t stream) 
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int DV>
 static hipError_t launch_bwd_bf16(BwdParams p, const AttnArgs& a, hipStream_t stream) {
-  p.nqb = (p.N + BwdCfg<D>::BQ - 1) / BwdCfg<D>::BQ;
+  using C = BwdCfg<D, DV>;
+  p.nqb = (p.N + C::BQ - 1) / C::BQ;
   // the dQ pass also writes delta and the base-2 LSE the dK/dV pass reads
   const hipError_t e = launch_bwd_dq(a, stream);
   if (e != hipSuccess) return e;
-  const long long grid = (long long)p.B * p.H * p.nkb * BwdCfg<D>::NSPLIT;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  const long long grid = (long long)p.B * p.H * p.nkb * C::NSPLIT;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, DV>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -695,11 +719,11 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.nkb = (a.N + kBwdBlockK - 1) / kBwdBlockK;
   p.nkb64 = (a.N + kTableBlock - 1) / kTableBlock;
   if (a.is_bf16) {
-    switch (a.d) {
-      case 64: return launch_bwd_bf16<64>(p, a, stream);
-      case 128: return launch_bwd_bf16<128>(p, a, stream);
-      case 256: return launch_bwd_bf16<256>(p, a, stream);
-    }
+    // the bf16 (d, dv) pairs compiled in (kept in step with bf16_dims())
+    if (a.d == 64 && a.dv == 64) return launch_bwd_bf16<64, 64>(p, a, stream);
+    if (a.d == 128 && a.dv == 128) return launch_bwd_bf16<128, 128>(p, a, stream);
+    if (a.d == 256 && a.dv == 256) return launch_bwd_bf16<256, 256>(p, a, stream);
+    if (a.d == 192 && a.dv == 128) return launch_bwd_bf16<192, 128>(p, a, stream);
   } else {
     switch (a.d) {
       case 64: return launch_bwd_f32<64>(p, stream);

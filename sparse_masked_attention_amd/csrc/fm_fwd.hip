@@ -95,21 +95,27 @@ __device__ inline void mask_block(f32x16& s, const FM_LDS int* vl, int kl0, int 
 constexpr int kModeFwd = 0;
 constexpr int kModeDq = 1;
 
-template <int D, int MODE>
+// D: head dim of Q and K; DV: head dim of V (and O, dO).
+template <int D, int DV, int MODE>
 struct QCfg {
   static constexpr int NW = 4;
   static constexpr int WR = 32;                           // query rows per wave
   static constexpr int BR = WR * NW;                      // query rows per workgroup
   static constexpr int BC = 64;                           // keys per tile
   // 32-key blocks per inner step (1 keeps registers within budget)
-  static constexpr int JBS = (D >= 256 || MODE == kModeDq) ? 1 : 2;
-  static constexpr int CH = D / 8;                        // 16-byte chunks per row
-  static constexpr int TILE = BC * D * 2;                 // bytes of one K or V tile
-  static constexpr int LOADS = TILE / (NW * 1024);        // per wave per tensor
+  static constexpr int JBS = (D > 128 || DV > 128 || MODE == kModeDq) ? 1 : 2;
+  static constexpr int CHK = D / 8;                       // 16-byte chunks per K row
+  static constexpr int CHV = DV / 8;                      // 16-byte chunks per V row
+  static constexpr int KT = BC * D * 2;                   // bytes of one K tile
+  static constexpr int VT = BC * DV * 2;                  // bytes of one V tile
+  static constexpr int LOADS_K = KT / (NW * 1024);        // per wave
+  static constexpr int LOADS_V = VT / (NW * 1024);
   static constexpr int VEC = 4 * BC * 4;                  // the tile's boundary vectors
-  static constexpr int STAGE = 2 * TILE + VEC;
+  static constexpr int STAGE = KT + VT + VEC;
   static constexpr int LIST = 1024;                       // compacted tile list entries
-  static constexpr int LOADS_PER_TILE = 2 * LOADS + 1;    // waves 0-3 (they stage a vector)
+  static constexpr int LOADS_PER_TILE = LOADS_K + LOADS_V + 1;  // waves 0-3 (they stage a vector)
+  // two workgroups per CU when both fit in LDS and 256 registers
+  static constexpr int WG_PER_CU = (D <= 128 && DV <= 128) ? 2 : 1;
 };
 
 // XOR swizzle of the 16-byte chunk index within a row: 32 consecutive rows
@@ -117,7 +123,9 @@ struct QCfg {
 // reads) both spread over the LDS banks.
 template <int D>
 __device__ inline int fswz(int row) {
-  if constexpr (D >= 128) return 4 * (row & 3) + ((row >> 2) & 3);
+  static_assert(D == 64 || D == 128 || D == 192 || D == 256, "row width");
+  if constexpr (D == 192) return (row >> 1) & 7;   // 24 chunks: stay inside each group of 8
+  else if constexpr (D >= 128) return 4 * (row & 3) + ((row >> 2) & 3);
   else return 4 * (row & 1) + ((row >> 1) & 3);
 }
 
@@ -127,9 +135,9 @@ __device__ inline int fswz(int row) {
 // since O and the row sum always use the same offset.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int MODE>
-__global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdParams p) {
-  using C = QCfg<D, MODE>;
+template <int D, int DV, int MODE>
+__global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf16_kernel(FwdParams p) {
+  using C = QCfg<D, DV, MODE>;
   constexpr bool DQ = MODE == kModeDq;
   // Two pipeline stages as separate LDS objects.
   __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
@@ -157,11 +165,12 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
   const int r1 = min(N, r0 + C::BR);
   const int wr0 = r0 + C::WR * w;                       // this wave's first row
   const int i = wr0 + l32;                              // this lane's row
-  const uint32_t tbytes = (uint32_t)N * D * 2;
+  const uint32_t tbytes = (uint32_t)N * D * 2;     // one head of Q or K
+  const uint32_t vbytes = (uint32_t)N * DV * 2;    // one head of V, O or dO
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(p.q) + slice * D, tbytes);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + slice * D, tbytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + slice * D, tbytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + slice * DV, vbytes);
   const long long vrow = ((long long)b * p.hm + hmi) * N;
   const int32_t* vecs[4] = {p.lts, p.lte, p.uts, p.ute};
   // each wave stages one of the four boundary vectors (absent ones read as 0)
@@ -176,22 +185,22 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
 #pragma unroll
   for (int c = 0; c < D / 16; ++c)
     qf[c] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(i * D + 16 * c + 8 * hh) * 2));
-  bf16x8 dof[DQ ? D / 16 : 1];
+  bf16x8 dof[DQ ? DV / 16 : 1];
   float row_lse2 = 0.f, row_delta = 0.f;
   if constexpr (DQ) {
     const __amdgpu_buffer_rsrc_t rdo =
-        make_rsrc(reinterpret_cast<const bf16*>(p.dout) + slice * D, tbytes);
+        make_rsrc(reinterpret_cast<const bf16*>(p.dout) + slice * DV, vbytes);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-      dof[c] = __builtin_bit_cast(bf16x8, buffer_load16(rdo, (uint32_t)(i * D + 16 * c + 8 * hh) * 2));
+    for (int c = 0; c < DV / 16; ++c)
+      dof[c] = __builtin_bit_cast(bf16x8, buffer_load16(rdo, (uint32_t)(i * DV + 16 * c + 8 * hh) * 2));
     // delta_i = dO_i . O_i: this lane holds half of row i (the chunks of
     // its half-wave), the other half-wave the rest
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<const bf16*>(p.o_in) + slice * D, tbytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<const bf16*>(p.o_in) + slice * DV, vbytes);
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     float dl = 0.f;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const bf16x8 oc = __builtin_bit_cast(bf16x8, buffer_load16(ro, (uint32_t)(i * D + 16 * c + 8 * hh) * 2));
+    for (int c = 0; c < DV / 16; ++c) {
+      const bf16x8 oc = __builtin_bit_cast(bf16x8, buffer_load16(ro, (uint32_t)(i * DV + 16 * c + 8 * hh) * 2));
 #pragma unroll
       for (int e = 0; e < 8; e += 2)
         dl = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{dof[c][e], dof[c][e + 1]}, bf16x2_t{oc[e], oc[e + 1]}, dl, false);
@@ -206,9 +215,10 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
     }
   }
 
-  f32x16 oacc[D / 32];           // O^T (forward) or dQ^T (dQ pass)
+  constexpr int NO = DQ ? D / 32 : DV / 32;   // 32-column blocks of the output
+  f32x16 oacc[NO];               // O^T (forward) or dQ^T (dQ pass)
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
+  for (int mb = 0; mb < NO; ++mb) oacc[mb] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
   if (tid < 3) wcount[tid] = 0;
@@ -223,30 +233,40 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
     const int kbase = kb * C::BC;
     FM_LDS char* st = (FM_LDS char*)(S ? stage1 : stage0);
 #pragma unroll
-    for (int u = 0; u < C::LOADS; ++u) {
-      const int g = (w * C::LOADS + u) * 64 + lane;   // physical chunk in the tile
-      const int row = g / C::CH, pch = g % C::CH;
-      const uint32_t off = (uint32_t)((kbase + row) * D + 8 * (pch ^ fswz<D>(row))) * 2;
-      load_lds16(rk, st + (w * C::LOADS + u) * 1024, off);
-      load_lds16(rv, st + C::TILE + (w * C::LOADS + u) * 1024, off);
+    for (int u = 0; u < C::LOADS_K; ++u) {
+      const int g = (w * C::LOADS_K + u) * 64 + lane;   // physical chunk in the K tile
+      const int row = g / C::CHK, pch = g % C::CHK;
+      load_lds16(rk, st + (w * C::LOADS_K + u) * 1024,
+                 (uint32_t)((kbase + row) * D + 8 * (pch ^ fswz<D>(row))) * 2);
+    }
+#pragma unroll
+    for (int u = 0; u < C::LOADS_V; ++u) {
+      const int g = (w * C::LOADS_V + u) * 64 + lane;   // physical chunk in the V tile
+      const int row = g / C::CHV, pch = g % C::CHV;
+      load_lds16(rv, st + C::KT + (w * C::LOADS_V + u) * 1024,
+                 (uint32_t)((kbase + row) * DV + 8 * (pch ^ fswz<DV>(row))) * 2);
     }
     // waves 0-3: 16 lanes x 16 bytes = one 64-key vector each
-    if (w < 4 && lane < 16) load_lds16(rvec, st + 2 * C::TILE + w * 256, (uint32_t)(kbase + 4 * lane) * 4);
+    if (w < 4 && lane < 16) load_lds16(rvec, st + C::KT + C::VT + w * 256, (uint32_t)(kbase + 4 * lane) * 4);
   };
 
-  // row operand read (32 rows of a tile at one 16-byte chunk)
-  auto row_read = [&](const FM_LDS char* t, int row, int chunk) {
-    return lds_read_b128(t + row * D * 2 + ((chunk ^ fswz<D>(row)) << 4));
+  using KW = std::integral_constant<int, D>;    // K tile width tag
+  using VW = std::integral_constant<int, DV>;   // V tile width tag
+  // row operand read (32 rows of a W-wide tile at one 16-byte chunk)
+  auto row_read = [&](auto w_c, const FM_LDS char* t, int row, int chunk) {
+    constexpr int W = decltype(w_c)::value;
+    return lds_read_b128(t + row * W * 2 + ((chunk ^ fswz<W>(row)) << 4));
   };
   // transposed operand read: for MFMA contraction chunk c (16 keys) and
   // column block mb, 4 consecutive keys of one column per lane, twice
-  auto tr_read = [&](const FM_LDS char* t, int c, int mb) {
+  auto tr_read = [&](auto w_c, const FM_LDS char* t, int c, int mb) {
+    constexpr int W = decltype(w_c)::value;
     const int sl = lane & 15;
     const int row_a = 16 * c + 4 * hh + (sl >> 2);
     const int row_b = row_a + 8;
     const int col = 32 * mb + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
-    const FM_LDS char* pa = t + row_a * D * 2 + (((col >> 3) ^ fswz<D>(row_a)) << 4) + (col & 7) * 2;
-    const FM_LDS char* pb = t + row_b * D * 2 + (((col >> 3) ^ fswz<D>(row_b)) << 4) + (col & 7) * 2;
+    const FM_LDS char* pa = t + row_a * W * 2 + (((col >> 3) ^ fswz<W>(row_a)) << 4) + (col & 7) * 2;
+    const FM_LDS char* pb = t + row_b * W * 2 + (((col >> 3) ^ fswz<W>(row_b)) << 4) + (col & 7) * 2;
     return cat(lds_read_tr(pa), lds_read_tr(pb));
   };
 
@@ -257,8 +277,8 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
     if (wc == 0) return;
     const int kbase = kb * C::BC;
     const FM_LDS char* kst = (const FM_LDS char*)(S ? stage1 : stage0);
-    const FM_LDS char* vst = kst + C::TILE;
-    const FM_LDS int* vl = (const FM_LDS int*)(kst + 2 * C::TILE);
+    const FM_LDS char* vst = kst + C::KT;
+    const FM_LDS int* vl = (const FM_LDS int*)(kst + C::KT + C::VT);
     constexpr int JBS = C::JBS;
     if (wc == 1) {
       // one key per lane: which of this wave's 32 rows the mask hides for it
@@ -294,10 +314,9 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
         const int row = jb * 32 + l32;
         // S^T = K Q^T + bias, dP^T = V dO^T
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          s = mfma32(row_read(kst, row, 2 * c + hh), qf[c], s);
-          dp = mfma32(row_read(vst, row, 2 * c + hh), dof[c], dp);
-        }
+        for (int c = 0; c < D / 16; ++c) s = mfma32(row_read(KW{}, kst, row, 2 * c + hh), qf[c], s);
+#pragma unroll
+        for (int c = 0; c < DV / 16; ++c) dp = mfma32(row_read(VW{}, vst, row, 2 * c + hh), dof[c], dp);
         // dS = P (dP - delta) with P = exp2(S * scale * log2e - LSE2)
         bf16x8 pf[2];
 #pragma unroll
@@ -309,7 +328,7 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-          for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32(tr_read(kst, 2 * jb + cc, mb), pf[cc], oacc[mb]);
+          for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32(tr_read(KW{}, kst, 2 * jb + cc, mb), pf[cc], oacc[mb]);
       }
     } else {
 #pragma unroll
@@ -322,7 +341,7 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
       for (int jj = 0; jj < JBS; ++jj) {
         const int row = (hk * JBS + jj) * 32 + l32;
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) s[jj] = mfma32(row_read(kst, row, 2 * c + hh), qf[c], s[jj]);
+        for (int c = 0; c < D / 16; ++c) s[jj] = mfma32(row_read(KW{}, kst, row, 2 * c + hh), qf[c], s[jj]);
       }
       bf16x8 pf[2 * JBS];
       float mx = max_acc(s);
@@ -334,7 +353,7 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
         const float alpha = m_new == kNegInf ? 1.f : fast_exp2((m_run - m_new) * p.sl2);
         l_run *= alpha;
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+        for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] *= alpha;
         m_run = m_new;
       }
       const float msl = (m_run == kNegInf ? 0.f : m_run) * p.sl2;
@@ -354,7 +373,7 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
       for (int cc = 0; cc < 2 * JBS; ++cc) {
         const int c = 2 * JBS * hk + cc;
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32(tr_read(vst, c, mb), pf[cc], oacc[mb]);
+        for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] = mfma32(tr_read(VW{}, vst, c, mb), pf[cc], oacc[mb]);
       }
     }
     }
@@ -440,9 +459,9 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void qmajor_bf16_kernel(FwdP
     const float lt = sum_x32(l_run);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (i < N) {
-      bf16* og = reinterpret_cast<bf16*>(p.o) + (slice + i) * D;
+      bf16* og = reinterpret_cast<bf16*>(p.o) + (slice + i) * DV;
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
+      for (int mb = 0; mb < DV / 32; ++mb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           bf16x4 v4;
@@ -607,13 +626,23 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------- launch
-template <int D, int MODE>
+template <int D, int DV, int MODE>
 static hipError_t launch_qmajor(FwdParams p, hipStream_t stream) {
-  using C = QCfg<D, MODE>;
+  using C = QCfg<D, DV, MODE>;
   p.nqb = (p.N + C::BR - 1) / C::BR;
   const long long grid = (long long)p.B * p.H * p.nqb;
-  hipLaunchKernelGGL((qmajor_bf16_kernel<D, MODE>), dim3((unsigned)grid), dim3(C::NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((qmajor_bf16_kernel<D, DV, MODE>), dim3((unsigned)grid), dim3(C::NW * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+// the bf16 (d, dv) pairs compiled in (kept in step with bf16_dims())
+template <int MODE>
+static hipError_t dispatch_qmajor(int d, int dv, const FwdParams& p, hipStream_t stream) {
+  if (d == 64 && dv == 64) return launch_qmajor<64, 64, MODE>(p, stream);
+  if (d == 128 && dv == 128) return launch_qmajor<128, 128, MODE>(p, stream);
+  if (d == 256 && dv == 256) return launch_qmajor<256, 256, MODE>(p, stream);
+  if (d == 192 && dv == 128) return launch_qmajor<192, 128, MODE>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 template <int D>
@@ -649,11 +678,7 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
   p.sl2 = a.scale * kLog2e;
   p.nkb = (a.N + kFwdBlockK - 1) / kFwdBlockK;
   if (a.is_bf16) {
-    switch (a.d) {
-      case 64: return launch_qmajor<64, kModeFwd>(p, stream);
-      case 128: return launch_qmajor<128, kModeFwd>(p, stream);
-      case 256: return launch_qmajor<256, kModeFwd>(p, stream);
-    }
+    return dispatch_qmajor<kModeFwd>(a.d, a.dv, p, stream);
   } else {
     switch (a.d) {
       case 64: return launch_fwd_f32<64>(p, stream);
@@ -695,12 +720,7 @@ hipError_t launch_bwd_dq(const AttnArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.sl2 = a.scale * kLog2e;
   p.nkb = (a.N + kFwdBlockK - 1) / kFwdBlockK;
-  switch (a.d) {
-    case 64: return launch_qmajor<64, kModeDq>(p, stream);
-    case 128: return launch_qmajor<128, kModeDq>(p, stream);
-    case 256: return launch_qmajor<256, kModeDq>(p, stream);
-  }
-  return hipErrorInvalidValue;
+  return dispatch_qmajor<kModeDq>(a.d, a.dv, p, stream);
 }
 
 }  // namespace fm

@@ -18,6 +18,12 @@ constexpr int kBwdBlockK = 128;
 // backward query-block height: 64 rows for bf16 with d <= 128, else 32
 inline int bwd_block_q(int d, int is_bf16) { return (is_bf16 && d <= 128) ? 64 : 32; }
 
+// Head dims with kernels compiled in: (d, dv) pairs for bf16, d == dv for fp32.
+inline bool bf16_dims(int d, int dv) {
+  return (d == dv && (d == 64 || d == 128 || d == 256)) || (d == 192 && dv == 128);
+}
+inline bool fp32_dims(int d, int dv) { return d == dv && (d == 64 || d == 128); }
+
 struct MaskArgs {
   const int32_t* lts;  // [B, hm, N] or nullptr
   const int32_t* lte;
