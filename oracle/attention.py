@@ -19,8 +19,11 @@ Readings of points the pages leave open:
   * a row with every key masked outputs 0, its logsumexp is -inf and it
     contributes no gradient;
   * the scale is 1/sqrt(d) with d the Q/K head dim (not the V head dim);
-  * lts None -> no lower interval; lte None -> LTE = N;
-    uts/ute None (non-causal) -> no upper interval.
+  * lts None -> no lower interval; lte None -> LTE = the number of query
+    rows; uts/ute None (non-causal) -> no upper interval;
+  * with Nq query rows and Nk keys (one context-parallel rank's share of the
+    rows, FlashMask-3 abstract) the vectors have Nk entries and hold bounds
+    on the Nq local rows; the causal test stays j > i in local indices.
 
 Vectors are [B, Hm, N] with Hm in {1, H}; head h uses mask row h if Hm == H,
 else row 0.
@@ -46,20 +49,22 @@ def mask_row(vec: Optional[np.ndarray], b: int, h: int) -> Optional[np.ndarray]:
 
 
 def dense_mask(n: int, causal: bool, lts=None, lte=None, uts=None, ute=None,
-               rows: Optional[np.ndarray] = None) -> np.ndarray:
+               rows: Optional[np.ndarray] = None, n_rows: Optional[int] = None) -> np.ndarray:
     """Boolean masked[i, j] for rows i (default all) and all columns j.
 
-    Arguments are the [N] vectors of one (batch, head). Follows the interval
-    test stated in the module docstring, term by term.
+    Arguments are the [n] vectors of one (batch, head): n keys (columns);
+    there are n_rows query rows (default n). Follows the interval test stated
+    in the module docstring, term by term.
     """
-    i = np.arange(n, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    nr = n if n_rows is None else int(n_rows)
+    i = np.arange(nr, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
     I = i[:, None]
     J = np.arange(n, dtype=np.int64)[None, :]
     m = np.zeros((I.shape[0], n), dtype=bool)
     if causal:
         m |= J > I
     if lts is not None:
-        end = np.full(n, n, np.int64) if lte is None else np.asarray(lte, np.int64)
+        end = np.full(n, nr, np.int64) if lte is None else np.asarray(lte, np.int64)
         m |= (np.asarray(lts, np.int64)[None, :] <= I) & (I < end[None, :])
     if not causal and uts is not None and ute is not None:
         m |= (np.asarray(uts, np.int64)[None, :] <= I) & (I < np.asarray(ute, np.int64)[None, :])
@@ -92,20 +97,22 @@ def forward_rows(q, k, v, n, causal, lts=None, lte=None, uts=None, ute=None,
                  rows=None, scale=None, chunk: int = 1024):
     """Forward of one (batch, head) for the given query rows.
 
-    q [N, d], k [N, d], v [N, dv] (any float dtype, widened exactly to fp64).
-    Returns (O [R, dv], lse [R]). Rows are processed in chunks so that long
-    sequences never hold an N x N matrix.
+    q [Nq, d], k [n, d], v [n, dv] (any float dtype, widened exactly to fp64);
+    n is the number of keys, the query rows number q.shape[0]. Returns
+    (O [R, dv], lse [R]). Rows are processed in chunks so that long sequences
+    never hold an Nq x n matrix.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     sc = _scale(q.shape[-1], scale)
-    rows = np.arange(n) if rows is None else np.asarray(rows, np.int64)
+    nq = q.shape[0]
+    rows = np.arange(nq) if rows is None else np.asarray(rows, np.int64)
     o = np.zeros((rows.shape[0], v.shape[-1]))
     lse = np.zeros(rows.shape[0])
     for c0 in range(0, rows.shape[0], chunk):
         r = rows[c0:c0 + chunk]
-        msk = dense_mask(n, causal, lts, lte, uts, ute, rows=r)
+        msk = dense_mask(n, causal, lts, lte, uts, ute, rows=r, n_rows=nq)
         P, l = softmax_probs(q[r], k, msk, sc)
         o[c0:c0 + chunk] = P @ v
         lse[c0:c0 + chunk] = l
@@ -114,18 +121,20 @@ def forward_rows(q, k, v, n, causal, lts=None, lte=None, uts=None, ute=None,
 
 def forward(q, k, v, causal, lts=None, lte=None, uts=None, ute=None,
             scale=None, heads=None) -> Tuple[np.ndarray, np.ndarray]:
-    """O [B,H,N,dv] and logsumexp [B,H,N] (natural log, scale included).
+    """O [B,H,Nq,dv] and logsumexp [B,H,Nq] (natural log, scale included).
 
+    q [B,H,Nq,d], k [B,H,Nk,d], v [B,H,Nk,dv], vectors [B,Hm,Nk].
     ``heads``: optional list of (b, h) pairs to evaluate; other entries stay 0.
     """
-    B, H, N, _ = q.shape
+    B, H, Nq, _ = q.shape
+    Nk = k.shape[2]
     dv = v.shape[-1]
-    o = np.zeros((B, H, N, dv))
-    lse = np.zeros((B, H, N))
+    o = np.zeros((B, H, Nq, dv))
+    lse = np.zeros((B, H, Nq))
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:
         o[b, h], lse[b, h] = forward_rows(
-            q[b, h], k[b, h], v[b, h], N, causal,
+            q[b, h], k[b, h], v[b, h], Nk, causal,
             mask_row(lts, b, h), mask_row(lte, b, h),
             mask_row(uts, b, h), mask_row(ute, b, h), scale=scale)
     return o, lse
@@ -140,11 +149,12 @@ def backward(q, k, v, do, causal, lts=None, lte=None, uts=None, ute=None,
       dK = scale dS^T Q.
     Rows with every key masked have P = 0 and so contribute nothing.
     """
-    B, H, N, d = q.shape
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
     dv_ = v.shape[-1]
-    dq = np.zeros((B, H, N, d))
-    dk = np.zeros((B, H, N, d))
-    dvv = np.zeros((B, H, N, dv_))
+    dq = np.zeros((B, H, Nq, d))
+    dk = np.zeros((B, H, Nk, d))
+    dvv = np.zeros((B, H, Nk, dv_))
     sc = _scale(d, scale)
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:
@@ -152,8 +162,8 @@ def backward(q, k, v, do, causal, lts=None, lte=None, uts=None, ute=None,
         K = np.asarray(k[b, h], np.float64)
         V = np.asarray(v[b, h], np.float64)
         dO = np.asarray(do[b, h], np.float64)
-        msk = dense_mask(N, causal, mask_row(lts, b, h), mask_row(lte, b, h),
-                         mask_row(uts, b, h), mask_row(ute, b, h))
+        msk = dense_mask(Nk, causal, mask_row(lts, b, h), mask_row(lte, b, h),
+                         mask_row(uts, b, h), mask_row(ute, b, h), n_rows=Nq)
         P, _ = softmax_probs(Q, K, msk, sc)
         del msk
         dvv[b, h] = P.T @ dO

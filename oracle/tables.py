@@ -34,14 +34,15 @@ def _full(vec, B, hm, n, fill):
     return np.asarray(vec, np.int64)
 
 
-def _neutral(lts, lte, uts, ute, B, hm, n):
-    """The four [B, Hm, N] vectors with neutral values where one is missing."""
+def _neutral(lts, lte, uts, ute, B, hm, n, n_rows):
+    """The four [B, Hm, n] vectors with neutral values where one is missing
+    (the empty lower interval is [n_rows, n_rows), n_rows query rows)."""
     if lts is None:
-        LTS = np.full((B, hm, n), n, np.int64)
-        LTE = np.full((B, hm, n), n, np.int64)
+        LTS = np.full((B, hm, n), n_rows, np.int64)
+        LTE = np.full((B, hm, n), n_rows, np.int64)
     else:
         LTS = np.asarray(lts, np.int64)
-        LTE = _full(lte, B, hm, n, n)
+        LTE = _full(lte, B, hm, n, n_rows)
     if uts is None or ute is None:
         UTS = np.zeros((B, hm, n), np.int64)
         UTE = np.zeros((B, hm, n), np.int64)
@@ -51,14 +52,15 @@ def _neutral(lts, lte, uts, ute, B, hm, n):
     return LTS, LTE, UTS, UTE
 
 
-def kblock_minmax(B, hm, n, block, lts=None, lte=None, uts=None, ute=None):
-    """int32 [B, Hm, ceil(N/block), 8] table.
+def kblock_minmax(B, hm, n, block, lts=None, lte=None, uts=None, ute=None, n_rows=None):
+    """int32 [B, Hm, ceil(n/block), 8] table over n key columns.
 
     Entry order: LTS min, LTS max, LTE min, LTE max, UTS min, UTS max,
-    UTE min, UTE max, each over columns [kb*block, min(N, (kb+1)*block)).
+    UTE min, UTE max, each over columns [kb*block, min(n, (kb+1)*block)).
+    Missing vectors take neutral values for n_rows query rows (default n).
     Plain loops over key blocks.
     """
-    vecs = _neutral(lts, lte, uts, ute, B, hm, n)
+    vecs = _neutral(lts, lte, uts, ute, B, hm, n, n if n_rows is None else int(n_rows))
     nkb = (n + block - 1) // block
     out = np.zeros((B, hm, nkb, 8), np.int64)
     for kb in range(nkb):
@@ -70,19 +72,20 @@ def kblock_minmax(B, hm, n, block, lts=None, lte=None, uts=None, ute=None):
     return out.astype(np.int32)
 
 
-def classify(table, n, block_q, block_k, causal):
-    """int8 [B, Hm, ceil(N/block_q), ceil(N/block_k)] tile classes.
+def classify(table, n, block_q, block_k, causal, n_rows=None):
+    """int8 [B, Hm, ceil(n_rows/block_q), ceil(n/block_k)] tile classes.
 
-    ``table`` must be the kblock_minmax table at granularity block_k. The rule
-    of the module docstring is evaluated for every (query block, key block)
-    pair at once with numpy broadcasting: rows index query blocks, columns key
-    blocks.
+    ``table`` must be the kblock_minmax table at granularity block_k over n
+    key columns; there are n_rows query rows (default n). The rule of the
+    module docstring is evaluated for every (query block, key block) pair at
+    once with numpy broadcasting: rows index query blocks, columns key blocks.
     """
     t = np.asarray(table, np.int64)
     B, hm, nkb, _ = t.shape
-    nqb = (n + block_q - 1) // block_q
+    nr = n if n_rows is None else int(n_rows)
+    nqb = (nr + block_q - 1) // block_q
     r0 = (np.arange(nqb, dtype=np.int64) * block_q)[:, None]
-    r1 = np.minimum(n, r0 + block_q)
+    r1 = np.minimum(nr, r0 + block_q)
     c0 = (np.arange(nkb, dtype=np.int64) * block_k)[None, :]
     c1 = np.minimum(n, c0 + block_k)
     out = np.zeros((B, hm, nqb, nkb), np.int8)
