@@ -153,6 +153,71 @@ fm_status_t flashmask_bwd(const void* q, const void* k, const void* v,
                           void* dq, void* dk, void* dv_out, int64_t* tile_counts,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Nq query rows against Nk keys (one context-parallel rank's share of the
+ * rows: FlashMask-3 abstract). Same contracts as the entry points above with
+ * N split in two: Q, O, dO, dQ are [B,H,Nq,*], logsumexp [B,H,Nq]; K, V, dK,
+ * dV are [B,H,Nk,*]; the mask vectors are [B,hm,Nk] and hold bounds on the Nq
+ * rows (a missing lte means LTE = Nq; the causal test is j > i). The table is
+ * [B,hm,ceil(Nk/block_k),8] and the class map [B,hm,ceil(Nq/block_q),
+ * ceil(Nk/block_k)]. Nk == 0 gives O = 0, LSE = -inf, dQ = 0; Nq == 0 gives
+ * dK = dV = 0. The entry points above are these with Nq = Nk = N.
+ */
+size_t flashmask_workspace_size_qk(int is_bwd, int B, int H, int Nq, int Nk, int d, int dv,
+                                   int hm, fm_dtype_t dtype);
+
+fm_status_t flashmask_tile_classify_qk(const int32_t* lts, const int32_t* lte,
+                                       const int32_t* uts, const int32_t* ute,
+                                       int B, int hm, int Nq, int Nk, int causal,
+                                       int block_q, int block_k,
+                                       int32_t* kblock_minmax, int8_t* tile_class,
+                                       void* stream);
+
+fm_status_t flashmask_fwd_qk(const void* q, const void* k, const void* v,
+                             const int32_t* lts, const int32_t* lte,
+                             const int32_t* uts, const int32_t* ute, int hm,
+                             const int32_t* kblock_minmax,
+                             int B, int H, int Nq, int Nk, int d, int dv, fm_dtype_t dtype,
+                             int causal, float softmax_scale,
+                             void* o, float* lse, int64_t* tile_counts,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+fm_status_t flashmask_bwd_qk(const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const void* dout,
+                             const int32_t* lts, const int32_t* lte,
+                             const int32_t* uts, const int32_t* ute, int hm,
+                             const int32_t* kblock_minmax,
+                             int B, int H, int Nq, int Nk, int d, int dv, fm_dtype_t dtype,
+                             int causal, float softmax_scale,
+                             void* dq, void* dk, void* dv_out, int64_t* tile_counts,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Largest nchunks flashmask_localize accepts. */
+int flashmask_max_chunks(void);
+
+/*
+ * Localise the mask to one rank's query rows (FlashMask-3 abstract: each rank
+ * localises the column-wise mask without communication). The rank holds the
+ * global rows of `nchunks` chunks [chunks[2c], chunks[2c+1]) (HOST pointer,
+ * int32 pairs; sorted, disjoint, non-empty, inside [0, n_rows]; at most
+ * flashmask_max_chunks()), in that order as its local rows 0..Nq-1. Input:
+ * the global vectors [B,hm,Nk] (same NULL conventions as above, bounds on
+ * n_rows global rows). Output (device, [B,hm,Nk] each, all four written):
+ * the vectors of the same mask restricted to the local rows, non-causal:
+ *     local(t) = sum_c clamp(t - q0_c, 0, q1_c - q0_c)
+ *     LTS', LTE' = local(LTS), local(LTE)  (no lower interval: Nq, Nq)
+ *     causal:     UTS', UTE' = 0, local(j)
+ *     non-causal: UTS', UTE' = local(UTS), local(UTE)  (none: 0, 0)
+ * Integer work: bit-exact. Pass the outputs with causal = 0 and the rank's
+ * Q rows (Nq = total chunk length) to flashmask_fwd_qk / flashmask_bwd_qk.
+ */
+fm_status_t flashmask_localize(const int32_t* lts, const int32_t* lte,
+                               const int32_t* uts, const int32_t* ute,
+                               int B, int hm, int Nk, int n_rows, int causal,
+                               const int32_t* chunks, int nchunks,
+                               int32_t* lts_out, int32_t* lte_out,
+                               int32_t* uts_out, int32_t* ute_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ from typing import Optional
 import torch
 
 __all__ = ["FlashMaskError", "Mask", "lib", "status_string", "table_block", "tile_shape",
-           "workspace_size", "tile_classify", "fwd", "bwd", "LIB_PATH"]
+           "workspace_size", "tile_classify", "fwd", "bwd", "localize", "max_chunks", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libflashmask.so")
 
@@ -41,6 +41,17 @@ _SIGNATURES = {
     "flashmask_bwd": (_c_int, [_c_void_p] * 6 + [_c_void_p] * 4 + [_c_int, _c_void_p]
                       + [_c_int] * 5 + [_c_int, _c_int, _c_float]
                       + [_c_void_p] * 4 + [_c_void_p, _c_size_t, _c_void_p]),
+    "flashmask_workspace_size_qk": (_c_size_t, [_c_int] * 8 + [_c_int]),
+    "flashmask_tile_classify_qk": (_c_int, [_c_void_p] * 4 + [_c_int] * 7 + [_c_void_p, _c_void_p, _c_void_p]),
+    "flashmask_fwd_qk": (_c_int, [_c_void_p] * 3 + [_c_void_p] * 4 + [_c_int, _c_void_p]
+                         + [_c_int] * 6 + [_c_int, _c_int, _c_float]
+                         + [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    "flashmask_bwd_qk": (_c_int, [_c_void_p] * 6 + [_c_void_p] * 4 + [_c_int, _c_void_p]
+                         + [_c_int] * 6 + [_c_int, _c_int, _c_float]
+                         + [_c_void_p] * 4 + [_c_void_p, _c_size_t, _c_void_p]),
+    "flashmask_max_chunks": (_c_int, []),
+    "flashmask_localize": (_c_int, [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p, _c_int]
+                           + [_c_void_p] * 4 + [_c_void_p]),
 }
 
 _lib = None
@@ -83,13 +94,19 @@ def tile_shape(is_bwd: bool, d: int, dtype: torch.dtype):
     return bq.value, bk.value
 
 
-def workspace_size(is_bwd: bool, B, H, N, d, dv, hm, dtype: torch.dtype) -> int:
-    return int(lib().flashmask_workspace_size(int(is_bwd), B, H, N, d, dv, hm, _dtype_code(dtype)))
+def workspace_size(is_bwd: bool, B, H, N, d, dv, hm, dtype: torch.dtype, Nk: Optional[int] = None) -> int:
+    """Workspace bytes; N query rows and Nk keys (default Nk = N)."""
+    nk = N if Nk is None else Nk
+    return int(lib().flashmask_workspace_size_qk(int(is_bwd), B, H, N, nk, d, dv, hm, _dtype_code(dtype)))
+
+
+def max_chunks() -> int:
+    return int(lib().flashmask_max_chunks())
 
 
 @dataclass
 class Mask:
-    """The four int32 boundary vectors [B, hm, N] on the device (None = absent)."""
+    """The four int32 boundary vectors [B, hm, Nk] on the device (None = absent)."""
     lts: Optional[torch.Tensor]
     lte: Optional[torch.Tensor]
     uts: Optional[torch.Tensor]
@@ -144,20 +161,22 @@ def _mask_ptrs(mask: Mask):
 
 
 def tile_classify(mask: Mask, B: int, N: int, block_q: int, block_k: int, classes: bool = True,
-                  table: Optional[torch.Tensor] = None):
-    """(table int32 [B,hm,ceil(N/block_k),8], classes int8 [B,hm,nqb,nkb] or None).
+                  table: Optional[torch.Tensor] = None, Nk: Optional[int] = None):
+    """(table int32 [B,hm,ceil(Nk/block_k),8], classes int8 [B,hm,nqb,nkb] or None)
+    for N query rows and Nk keys (default Nk = N).
 
     ``table``: optional preallocated output for the table."""
     dev = next(t for t in (mask.lts, mask.lte, mask.uts, mask.ute) if t is not None).device \
         if any(t is not None for t in (mask.lts, mask.lte, mask.uts, mask.ute)) else torch.device("cuda")
     hm = mask.hm
-    nkb = -(-N // block_k)
+    nk = N if Nk is None else Nk
+    nkb = -(-nk // block_k)
     nqb = -(-N // block_q)
     if table is None:
         table = torch.empty((B, hm, nkb, 8), dtype=torch.int32, device=dev)
     cls = torch.empty((B, hm, nqb, nkb), dtype=torch.int8, device=dev) if classes else None
-    st = lib().flashmask_tile_classify(*_mask_ptrs(mask), B, hm, N, int(mask.causal), block_q, block_k,
-                                       _ptr(table), _ptr(cls), _stream(dev))
+    st = lib().flashmask_tile_classify_qk(*_mask_ptrs(mask), B, hm, N, nk, int(mask.causal), block_q,
+                                          block_k, _ptr(table), _ptr(cls), _stream(dev))
     _check("flashmask_tile_classify", st)
     return table, cls
 
@@ -166,31 +185,37 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask, scale: Op
         table: Optional[torch.Tensor] = None, tile_counts: Optional[torch.Tensor] = None,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None):
-    """O [B,H,N,dv] (q's dtype) and logsumexp [B,H,N] float32."""
+    """O [B,H,Nq,dv] (q's dtype) and logsumexp [B,H,Nq] float32.
+
+    q [B,H,Nq,d], k [B,H,Nk,d], v [B,H,Nk,dv]; the mask vectors have Nk
+    entries (Nq == Nk is the plain case)."""
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     dv = v.shape[-1]
-    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype or v.dtype != q.dtype:
+    if (k.shape[:2] != q.shape[:2] or k.shape[-1] != d or v.shape[:3] != k.shape[:3]
+            or k.dtype != q.dtype or v.dtype != q.dtype):
         raise ValueError("q, k, v shapes/dtypes disagree")
     o = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    ws_bytes = workspace_size(False, B, H, N, d, dv, mask.hm, q.dtype)
+    ws_bytes = workspace_size(False, B, H, N, d, dv, mask.hm, q.dtype, Nk=Nk)
     ws = workspace
     if ws is None and table is None and ws_bytes > 0:
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    st = lib().flashmask_fwd(_ptr(q), _ptr(k), _ptr(v), *_mask_ptrs(mask), mask.hm, _ptr(table),
-                             B, H, N, d, dv, _dtype_code(q.dtype), int(mask.causal),
-                             0.0 if scale is None else float(scale),
-                             _ptr(o), _ptr(l), _ptr(tile_counts), _ptr(ws),
-                             0 if ws is None else ws.numel(), _stream(q.device))
-    _check("flashmask_fwd", st)
+    st = lib().flashmask_fwd_qk(_ptr(q), _ptr(k), _ptr(v), *_mask_ptrs(mask), mask.hm, _ptr(table),
+                                B, H, N, Nk, d, dv, _dtype_code(q.dtype), int(mask.causal),
+                                0.0 if scale is None else float(scale),
+                                _ptr(o), _ptr(l), _ptr(tile_counts), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(q.device))
+    _check("flashmask_fwd_qk", st)
     return o, l
 
 
 def bwd(q, k, v, o, lse, dout, mask: Mask, scale: Optional[float] = None,
         table: Optional[torch.Tensor] = None, tile_counts: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None, grads=None):
-    """(dQ, dK, dV) in q's dtype."""
+    """(dQ, dK, dV) in q's dtype (shapes as in fwd)."""
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     dv = v.shape[-1]
     if grads is None:
         dq = torch.empty_like(q)
@@ -198,16 +223,33 @@ def bwd(q, k, v, o, lse, dout, mask: Mask, scale: Optional[float] = None,
         dvv = torch.empty_like(v)
     else:
         dq, dk, dvv = grads
-    ws_bytes = workspace_size(True, B, H, N, d, dv, mask.hm, q.dtype)
+    ws_bytes = workspace_size(True, B, H, N, d, dv, mask.hm, q.dtype, Nk=Nk)
     ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    st = lib().flashmask_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
-                             *_mask_ptrs(mask), mask.hm, _ptr(table),
-                             B, H, N, d, dv, _dtype_code(q.dtype), int(mask.causal),
-                             0.0 if scale is None else float(scale),
-                             _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(tile_counts), _ptr(ws), ws.numel(),
-                             _stream(q.device))
-    _check("flashmask_bwd", st)
+    st = lib().flashmask_bwd_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                *_mask_ptrs(mask), mask.hm, _ptr(table),
+                                B, H, N, Nk, d, dv, _dtype_code(q.dtype), int(mask.causal),
+                                0.0 if scale is None else float(scale),
+                                _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(tile_counts), _ptr(ws), ws.numel(),
+                                _stream(q.device))
+    _check("flashmask_bwd_qk", st)
     return dq, dk, dvv
+
+
+def localize(mask: Mask, B: int, Nk: int, n_rows: int, chunks) -> Mask:
+    """The mask restricted to one rank's query rows, computed on the GPU by
+    flashmask_localize: chunks are (q0, q1) global row ranges, sorted and
+    disjoint; the result is non-causal with all four vectors [B, hm, Nk]."""
+    import numpy as np
+    c = np.ascontiguousarray(np.asarray(chunks, np.int32).reshape(-1, 2))
+    dev = next((t.device for t in (mask.lts, mask.lte, mask.uts, mask.ute) if t is not None),
+               torch.device("cuda"))
+    hm = mask.hm
+    outs = [torch.empty((B, hm, Nk), dtype=torch.int32, device=dev) for _ in range(4)]
+    st = lib().flashmask_localize(*_mask_ptrs(mask), B, hm, Nk, n_rows, int(mask.causal),
+                                  c.ctypes.data_as(ctypes.c_void_p), int(c.shape[0]),
+                                  *[_ptr(t) for t in outs], _stream(dev))
+    _check("flashmask_localize", st)
+    return Mask(outs[0], outs[1], outs[2], outs[3], False)
 
 
 def default_scale(d: int) -> float:

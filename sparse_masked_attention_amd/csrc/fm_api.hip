@@ -38,19 +38,19 @@ size_t table_bytes(int B, int hm, int N) {
 }
 
 // Checks shared by the attention entry points; FM_SUCCESS when usable.
-fm_status_t check_common(int B, int H, int N, int d, int dv, fm_dtype_t dtype, int hm,
-                         const int32_t* lts, const int32_t* lte, const int32_t* uts,
-                         const int32_t* ute, int causal) {
-  if (B < 0 || H < 0 || N < 0 || d <= 0 || dv <= 0 || hm < 1) return FM_ERROR_INVALID_VALUE;
+fm_status_t check_common(int B, int H, int Nq, int Nk, int d, int dv, fm_dtype_t dtype, int hm,
+                         const int32_t* uts, const int32_t* ute, int causal) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d <= 0 || dv <= 0 || hm < 1)
+    return FM_ERROR_INVALID_VALUE;
   if (dtype != FM_BF16 && dtype != FM_FP32) return FM_ERROR_INVALID_VALUE;
   if (H > 0 && hm != 1 && hm != H) return FM_ERROR_INVALID_VALUE;
   if (!causal && ((uts == nullptr) != (ute == nullptr))) return FM_ERROR_INVALID_VALUE;
-  (void)lts;
-  (void)lte;
   if (!supported(d, dv, dtype)) return FM_ERROR_NOT_SUPPORTED;
   // 32-bit buffer offsets address one (batch, head) slice of a tensor
-  if ((long long)N * d * (dtype == FM_BF16 ? 2 : 4) >= (1LL << 31)) return FM_ERROR_NOT_SUPPORTED;
-  if ((long long)B * H * ceil_div(N, 32) >= (1LL << 31)) return FM_ERROR_NOT_SUPPORTED;
+  const long long rows = Nq > Nk ? Nq : Nk;
+  const long long width = d > dv ? d : dv;
+  if (rows * width * (dtype == FM_BF16 ? 2 : 4) >= (1LL << 31)) return FM_ERROR_NOT_SUPPORTED;
+  if ((long long)B * H * ceil_div(rows, 32) >= (1LL << 31)) return FM_ERROR_NOT_SUPPORTED;
   return FM_SUCCESS;
 }
 
@@ -97,54 +97,67 @@ fm_status_t flashmask_tile_shape(int is_bwd, int d, fm_dtype_t dtype, int* block
   return FM_SUCCESS;
 }
 
-size_t flashmask_workspace_size(int is_bwd, int B, int H, int N, int d, int dv, int hm,
-                                fm_dtype_t dtype) {
-  if (B < 0 || H < 0 || N < 0 || hm <= 0 || d <= 0 || dv <= 0) return 0;
+size_t flashmask_workspace_size_qk(int is_bwd, int B, int H, int Nq, int Nk, int d, int dv, int hm,
+                                   fm_dtype_t dtype) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || hm <= 0 || d <= 0 || dv <= 0) return 0;
   if (!supported(d, dv, dtype)) return 0;
-  size_t bytes = align_up(table_bytes(B, hm, N));
+  size_t bytes = align_up(table_bytes(B, hm, Nk));
   if (is_bwd) {
-    bytes += 2 * align_up((size_t)B * H * N * sizeof(float));             // delta, base-2 LSE
+    bytes += 2 * align_up((size_t)B * H * Nq * sizeof(float));             // delta, base-2 LSE
     if (dtype == FM_FP32)
-      bytes += align_up((size_t)B * H * N * (size_t)d * sizeof(float));   // dQ accumulator
+      bytes += align_up((size_t)B * H * Nq * (size_t)d * sizeof(float));   // dQ accumulator
   }
   return bytes;
 }
 
-fm_status_t flashmask_tile_classify(const int32_t* lts, const int32_t* lte, const int32_t* uts,
-                                    const int32_t* ute, int B, int hm, int N, int causal,
-                                    int block_q, int block_k, int32_t* kblock_minmax,
-                                    int8_t* tile_class, void* stream) {
-  if (B < 0 || hm <= 0 || N < 0 || block_q < 1 || block_k < 1) return FM_ERROR_INVALID_VALUE;
+size_t flashmask_workspace_size(int is_bwd, int B, int H, int N, int d, int dv, int hm,
+                                fm_dtype_t dtype) {
+  return flashmask_workspace_size_qk(is_bwd, B, H, N, N, d, dv, hm, dtype);
+}
+
+fm_status_t flashmask_tile_classify_qk(const int32_t* lts, const int32_t* lte, const int32_t* uts,
+                                       const int32_t* ute, int B, int hm, int Nq, int Nk, int causal,
+                                       int block_q, int block_k, int32_t* kblock_minmax,
+                                       int8_t* tile_class, void* stream) {
+  if (B < 0 || hm <= 0 || Nq < 0 || Nk < 0 || block_q < 1 || block_k < 1) return FM_ERROR_INVALID_VALUE;
   if (!causal && ((uts == nullptr) != (ute == nullptr))) return FM_ERROR_INVALID_VALUE;
-  if ((long long)B * hm * N == 0) return FM_SUCCESS;
+  if ((long long)B * hm * Nk == 0) return FM_SUCCESS;   // no key column: no table, no tile
   if (kblock_minmax == nullptr || !aligned(kblock_minmax, 16)) return FM_ERROR_INVALID_VALUE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const fm::MaskArgs m = mask_args(lts, lte, uts, ute, hm, causal);
-  if (fm::launch_kblock_minmax(m, B, N, block_k, kblock_minmax, s) != hipSuccess) return FM_ERROR_HIP;
-  if (tile_class != nullptr) {
-    if (fm::launch_classify(kblock_minmax, B, hm, N, causal != 0, block_q, block_k, tile_class, s) !=
+  if (fm::launch_kblock_minmax(m, B, Nq, Nk, block_k, kblock_minmax, s) != hipSuccess) return FM_ERROR_HIP;
+  if (tile_class != nullptr && Nq > 0) {
+    if (fm::launch_classify(kblock_minmax, B, hm, Nq, Nk, causal != 0, block_q, block_k, tile_class, s) !=
         hipSuccess)
       return FM_ERROR_HIP;
   }
   return FM_SUCCESS;
 }
 
-fm_status_t flashmask_fwd(const void* q, const void* k, const void* v, const int32_t* lts,
-                          const int32_t* lte, const int32_t* uts, const int32_t* ute, int hm,
-                          const int32_t* kblock_minmax, int B, int H, int N, int d, int dv,
-                          fm_dtype_t dtype, int causal, float softmax_scale, void* o, float* lse,
-                          int64_t* tile_counts, void* workspace, size_t workspace_bytes,
-                          void* stream) {
-  fm_status_t st = check_common(B, H, N, d, dv, dtype, hm, lts, lte, uts, ute, causal);
+fm_status_t flashmask_tile_classify(const int32_t* lts, const int32_t* lte, const int32_t* uts,
+                                    const int32_t* ute, int B, int hm, int N, int causal,
+                                    int block_q, int block_k, int32_t* kblock_minmax,
+                                    int8_t* tile_class, void* stream) {
+  return flashmask_tile_classify_qk(lts, lte, uts, ute, B, hm, N, N, causal, block_q, block_k,
+                                    kblock_minmax, tile_class, stream);
+}
+
+fm_status_t flashmask_fwd_qk(const void* q, const void* k, const void* v, const int32_t* lts,
+                             const int32_t* lte, const int32_t* uts, const int32_t* ute, int hm,
+                             const int32_t* kblock_minmax, int B, int H, int Nq, int Nk, int d,
+                             int dv, fm_dtype_t dtype, int causal, float softmax_scale, void* o,
+                             float* lse, int64_t* tile_counts, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  fm_status_t st = check_common(B, H, Nq, Nk, d, dv, dtype, hm, uts, ute, causal);
   if (st != FM_SUCCESS) return st;
-  if ((long long)B * H * N == 0) return FM_SUCCESS;
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr)
-    return FM_ERROR_INVALID_VALUE;
+  if ((long long)B * H * Nq == 0) return FM_SUCCESS;
+  if (q == nullptr || o == nullptr || lse == nullptr) return FM_ERROR_INVALID_VALUE;
+  if (Nk > 0 && (k == nullptr || v == nullptr)) return FM_ERROR_INVALID_VALUE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
     return FM_ERROR_INVALID_VALUE;
   if (kblock_minmax != nullptr && !aligned(kblock_minmax, 16)) return FM_ERROR_INVALID_VALUE;
-  const size_t need = flashmask_workspace_size(0, B, H, N, d, dv, hm, dtype);
-  if (kblock_minmax == nullptr && (workspace == nullptr || workspace_bytes < need))
+  const size_t need = flashmask_workspace_size_qk(0, B, H, Nq, Nk, d, dv, hm, dtype);
+  if (kblock_minmax == nullptr && Nk > 0 && (workspace == nullptr || workspace_bytes < need))
     return FM_ERROR_WORKSPACE_TOO_SMALL;
   if (workspace != nullptr && !aligned(workspace, kAlign)) return FM_ERROR_INVALID_VALUE;
 
@@ -152,9 +165,9 @@ fm_status_t flashmask_fwd(const void* q, const void* k, const void* v, const int
   fm::AttnArgs a{};
   a.mask = mask_args(lts, lte, uts, ute, hm, causal);
   const int32_t* table = kblock_minmax;
-  if (table == nullptr) {
+  if (table == nullptr && Nk > 0) {
     int32_t* t = reinterpret_cast<int32_t*>(workspace);
-    if (fm::launch_kblock_minmax(a.mask, B, N, kTableBlock, t, s) != hipSuccess) return FM_ERROR_HIP;
+    if (fm::launch_kblock_minmax(a.mask, B, Nq, Nk, kTableBlock, t, s) != hipSuccess) return FM_ERROR_HIP;
     table = t;
   }
   a.q = q;
@@ -163,7 +176,8 @@ fm_status_t flashmask_fwd(const void* q, const void* k, const void* v, const int
   a.table = table;
   a.B = B;
   a.H = H;
-  a.N = N;
+  a.Nq = Nq;
+  a.Nk = Nk;
   a.d = d;
   a.dv = dv;
   a.is_bf16 = dtype == FM_BF16;
@@ -175,25 +189,38 @@ fm_status_t flashmask_fwd(const void* q, const void* k, const void* v, const int
   return FM_SUCCESS;
 }
 
-fm_status_t flashmask_bwd(const void* q, const void* k, const void* v, const void* o,
-                          const float* lse, const void* dout, const int32_t* lts,
+fm_status_t flashmask_fwd(const void* q, const void* k, const void* v, const int32_t* lts,
                           const int32_t* lte, const int32_t* uts, const int32_t* ute, int hm,
                           const int32_t* kblock_minmax, int B, int H, int N, int d, int dv,
-                          fm_dtype_t dtype, int causal, float softmax_scale, void* dq, void* dk,
-                          void* dv_out, int64_t* tile_counts, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  fm_status_t st = check_common(B, H, N, d, dv, dtype, hm, lts, lte, uts, ute, causal);
+                          fm_dtype_t dtype, int causal, float softmax_scale, void* o, float* lse,
+                          int64_t* tile_counts, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return flashmask_fwd_qk(q, k, v, lts, lte, uts, ute, hm, kblock_minmax, B, H, N, N, d, dv, dtype,
+                          causal, softmax_scale, o, lse, tile_counts, workspace, workspace_bytes,
+                          stream);
+}
+
+fm_status_t flashmask_bwd_qk(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, const int32_t* lts,
+                             const int32_t* lte, const int32_t* uts, const int32_t* ute, int hm,
+                             const int32_t* kblock_minmax, int B, int H, int Nq, int Nk, int d,
+                             int dv, fm_dtype_t dtype, int causal, float softmax_scale, void* dq,
+                             void* dk, void* dv_out, int64_t* tile_counts, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  fm_status_t st = check_common(B, H, Nq, Nk, d, dv, dtype, hm, uts, ute, causal);
   if (st != FM_SUCCESS) return st;
   if (!bwd_supported(d, dv, dtype)) return FM_ERROR_NOT_SUPPORTED;
-  if ((long long)B * H * N == 0) return FM_SUCCESS;
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
-      dout == nullptr || dq == nullptr || dk == nullptr || dv_out == nullptr)
+  if ((long long)B * H * (Nq > Nk ? Nq : Nk) == 0) return FM_SUCCESS;
+  // the query side (Q, O, LSE, dO, dQ) may be empty, or the key side (K, V, dK, dV)
+  if (Nq > 0 && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr))
+    return FM_ERROR_INVALID_VALUE;
+  if (Nk > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv_out == nullptr))
     return FM_ERROR_INVALID_VALUE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv_out, 16))
     return FM_ERROR_INVALID_VALUE;
   if (kblock_minmax != nullptr && !aligned(kblock_minmax, 16)) return FM_ERROR_INVALID_VALUE;
-  const size_t need = flashmask_workspace_size(1, B, H, N, d, dv, hm, dtype);
+  const size_t need = flashmask_workspace_size_qk(1, B, H, Nq, Nk, d, dv, hm, dtype);
   if (workspace == nullptr || workspace_bytes < need) return FM_ERROR_WORKSPACE_TOO_SMALL;
   if (!aligned(workspace, kAlign)) return FM_ERROR_INVALID_VALUE;
 
@@ -202,16 +229,16 @@ fm_status_t flashmask_bwd(const void* q, const void* k, const void* v, const voi
   fm::AttnArgs a{};
   a.mask = mask_args(lts, lte, uts, ute, hm, causal);
   const int32_t* table = kblock_minmax;
-  if (table == nullptr) {
+  if (table == nullptr && Nk > 0) {
     int32_t* t = reinterpret_cast<int32_t*>(ws);
-    if (fm::launch_kblock_minmax(a.mask, B, N, kTableBlock, t, s) != hipSuccess) return FM_ERROR_HIP;
+    if (fm::launch_kblock_minmax(a.mask, B, Nq, Nk, kTableBlock, t, s) != hipSuccess) return FM_ERROR_HIP;
     table = t;
   }
-  ws += align_up(table_bytes(B, hm, N));
+  ws += align_up(table_bytes(B, hm, Nk));
   a.delta = reinterpret_cast<float*>(ws);
-  ws += align_up((size_t)B * H * N * sizeof(float));
+  ws += align_up((size_t)B * H * Nq * sizeof(float));
   a.lse2 = reinterpret_cast<float*>(ws);
-  ws += align_up((size_t)B * H * N * sizeof(float));
+  ws += align_up((size_t)B * H * Nq * sizeof(float));
   a.dq_acc = dtype == FM_FP32 ? reinterpret_cast<float*>(ws) : nullptr;
   a.q = q;
   a.k = k;
@@ -222,7 +249,8 @@ fm_status_t flashmask_bwd(const void* q, const void* k, const void* v, const voi
   a.table = table;
   a.B = B;
   a.H = H;
-  a.N = N;
+  a.Nq = Nq;
+  a.Nk = Nk;
   a.d = d;
   a.dv = dv;
   a.is_bf16 = dtype == FM_BF16;
@@ -232,6 +260,42 @@ fm_status_t flashmask_bwd(const void* q, const void* k, const void* v, const voi
   a.dv_out = dv_out;
   a.tile_counts = reinterpret_cast<unsigned long long*>(tile_counts);
   if (fm::launch_bwd(a, s) != hipSuccess) return FM_ERROR_HIP;
+  return FM_SUCCESS;
+}
+
+fm_status_t flashmask_bwd(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, const int32_t* lts,
+                          const int32_t* lte, const int32_t* uts, const int32_t* ute, int hm,
+                          const int32_t* kblock_minmax, int B, int H, int N, int d, int dv,
+                          fm_dtype_t dtype, int causal, float softmax_scale, void* dq, void* dk,
+                          void* dv_out, int64_t* tile_counts, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return flashmask_bwd_qk(q, k, v, o, lse, dout, lts, lte, uts, ute, hm, kblock_minmax, B, H, N, N,
+                          d, dv, dtype, causal, softmax_scale, dq, dk, dv_out, tile_counts,
+                          workspace, workspace_bytes, stream);
+}
+
+int flashmask_max_chunks(void) { return fm::kMaxChunks; }
+
+fm_status_t flashmask_localize(const int32_t* lts, const int32_t* lte, const int32_t* uts,
+                               const int32_t* ute, int B, int hm, int Nk, int n_rows, int causal,
+                               const int32_t* chunks, int nchunks, int32_t* lts_out,
+                               int32_t* lte_out, int32_t* uts_out, int32_t* ute_out, void* stream) {
+  if (B < 0 || hm < 1 || Nk < 0 || n_rows < 0) return FM_ERROR_INVALID_VALUE;
+  if (!causal && ((uts == nullptr) != (ute == nullptr))) return FM_ERROR_INVALID_VALUE;
+  if (chunks == nullptr || nchunks < 1 || nchunks > fm::kMaxChunks) return FM_ERROR_INVALID_VALUE;
+  for (int i = 0; i < nchunks; ++i) {
+    const int a = chunks[2 * i], b = chunks[2 * i + 1];
+    if (a < 0 || b > n_rows || b <= a) return FM_ERROR_INVALID_VALUE;
+    if (i > 0 && a < chunks[2 * i - 1]) return FM_ERROR_INVALID_VALUE;
+  }
+  if ((long long)B * hm * Nk == 0) return FM_SUCCESS;
+  if (lts_out == nullptr || lte_out == nullptr || uts_out == nullptr || ute_out == nullptr)
+    return FM_ERROR_INVALID_VALUE;
+  const fm::MaskArgs m = mask_args(lts, lte, uts, ute, hm, causal);
+  if (fm::launch_localize(m, B, Nk, n_rows, chunks, nchunks, lts_out, lte_out, uts_out, ute_out,
+                          reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return FM_ERROR_HIP;
   return FM_SUCCESS;
 }
 

@@ -42,7 +42,7 @@ struct BwdParams {
   const int32_t* lte;
   const int32_t* uts;
   const int32_t* ute;
-  const int32_t* table;  // [B, hm, ceil(N/64), 8]
+  const int32_t* table;  // [B, hm, ceil(Nk/64), 8]
   float* dq_acc;     // fp32 path only
   float* delta;
   float* lse2;       // logsumexp in base-2 units; +inf for fully masked rows
@@ -50,7 +50,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   unsigned long long* counts;
-  int B, H, N, hm, causal;
+  int B, H, Nq, Nk, hm, causal;   // Nq query rows, Nk keys
   int has_lt, has_lte, has_ut;
   float scale, sl2;
   int nqb, nkb, nkb64;
@@ -63,7 +63,7 @@ struct BwdParams {
 // bf16 path computes delta and the base-2 LSE inside its dQ pass.)
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-  const long long rows = (long long)p.B * p.H * p.N;
+  const long long rows = (long long)p.B * p.H * p.Nq;
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int t = threadIdx.x & 15;
   float acc = 0.f;
@@ -186,21 +186,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int col0v = sp * C::DVO;             // first dV column
   const int b = bh / p.H, h = bh % p.H;
   const int hmi = p.hm == 1 ? 0 : h;
-  const int N = p.N;
-  const long long slice = (long long)bh * N;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const long long qslice = (long long)bh * Nq;    // rows of Q, dO, LSE, delta
+  const long long kslice = (long long)bh * Nk;    // rows of K, V, dK, dV
   const int c0 = kb * C::BKC;
-  const int c1 = min(N, c0 + C::BKC);
+  const int c1 = min(Nk, c0 + C::BKC);
   const int wc0 = c0 + C::KW * w;                // this wave's first key
   const int j = wc0 + l32;                        // this lane's key
-  const uint32_t tbytes = (uint32_t)N * D * 2;     // one head of Q or K
-  const uint32_t vbytes = (uint32_t)N * DV * 2;    // one head of V or dO
+  const uint32_t qbytes = (uint32_t)Nq * D * 2;    // one head of Q
+  const uint32_t kbytes = (uint32_t)Nk * D * 2;    // one head of K
+  const uint32_t vbytes = (uint32_t)Nk * DV * 2;   // one head of V
+  const uint32_t obytes = (uint32_t)Nq * DV * 2;   // one head of dO
 
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(p.q) + slice * D, tbytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + slice * D, tbytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + slice * DV, vbytes);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const bf16*>(p.dout) + slice * DV, vbytes);
-  const __amdgpu_buffer_rsrc_t rlse = make_rsrc(p.lse2 + slice, (uint32_t)N * 4);
-  const __amdgpu_buffer_rsrc_t rdel = make_rsrc(p.delta + slice, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(p.q) + qslice * D, qbytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + kslice * D, kbytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + kslice * DV, vbytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const bf16*>(p.dout) + qslice * DV, obytes);
+  const __amdgpu_buffer_rsrc_t rlse = make_rsrc(p.lse2 + qslice, (uint32_t)Nq * 4);
+  const __amdgpu_buffer_rsrc_t rdel = make_rsrc(p.delta + qslice, (uint32_t)Nq * 4);
 
   // K and V of this lane's key as the B operands of S = Q K^T and dP = dO V^T
   bf16x8 kB[D / 16], vB[DV / 16];
@@ -211,12 +214,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   for (int c = 0; c < DV / 16; ++c)
     vB[c] = __builtin_bit_cast(bf16x8, buffer_load16(rv, (uint32_t)(j * DV + 16 * c + 8 * hh) * 2));
   // this lane's key bounds (the element test needs nothing else)
-  const long long vrow = ((long long)b * p.hm + hmi) * N;
-  int k_lts = N, k_lte = N, k_uts = 0, k_ute = 0;
-  if (j < N) {
+  const long long vrow = ((long long)b * p.hm + hmi) * Nk;
+  int k_lts = Nq, k_lte = Nq, k_uts = 0, k_ute = 0;   // empty intervals
+  if (j < Nk) {
     if (p.has_lt) {
       k_lts = p.lts[vrow + j];
-      k_lte = p.has_lte ? p.lte[vrow + j] : N;
+      k_lte = p.has_lte ? p.lte[vrow + j] : Nq;
     }
     if (p.has_ut) {
       k_uts = p.uts[vrow + j];
@@ -276,11 +279,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib) {
         // masked rows of this lane's key among rows q0 + 32 ib + [0, 32)
-        // (rows past N too: their staged LSE is not +inf), shifted so that
+        // (rows past Nq too: their staged LSE is not +inf), shifted so that
         // bit 8 g + e is the row of register 4 g + e
         const int rb = q0 + 32 * ib;
-        const uint32_t mw = (key_row_mask(j, rb, N, causal, has_lt, has_ut, k_lts, k_lte, k_uts, k_ute) |
-                             row_bits(N, rb + 32, rb)) >> (4 * hh);
+        const uint32_t mw = (key_row_mask(j, rb, Nk, causal, has_lt, has_ut, k_lts, k_lte, k_uts, k_ute) |
+                             row_bits(Nq, rb + 32, rb)) >> (4 * hh);
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[ib][r] = ((mw >> (8 * (r / 4) + r % 4)) & 1u) ? kNegInf : 0.f;
       }
@@ -385,7 +388,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     unsigned entry = 0;
     bool valid = false;
     if (qb < p.nqb) {
-      const int r0 = qb * C::BQ, r1 = min(N, r0 + C::BQ);
+      const int r0 = qb * C::BQ, r1 = min(Nq, r0 + C::BQ);
       const int wgc = tile_class(kbnd, r0, r1, c0, c1, causal);
       cnt0 += wgc == 0;
       cnt1 += wgc == 1;
@@ -398,9 +401,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         for (int ww = 0; ww < C::NW; ++ww) {
           const int a0 = c0 + C::KW * ww;
           int cls = 0;
-          if (a0 < N) {
+          if (a0 < Nk) {
             const BlockBounds wb = load_bounds(table + (long long)(a0 / 64) * 8);
-            cls = tile_class(wb, r0, r1, a0, min(N, a0 + C::KW), causal);
+            cls = tile_class(wb, r0, r1, a0, min(Nk, a0 + C::KW), causal);
             if (ragged && cls == 2) cls = 1;
           }
           bits |= cls << (2 * ww);
@@ -450,13 +453,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   wait_vmcnt<0>();  // no load into LDS may still be in flight when the wave ends
   // --- write dK = scale * dS^T Q and dV for this wave's keys
-  if (wc0 < N) {
-    bf16* dkg = reinterpret_cast<bf16*>(p.dk) + slice * D;
-    bf16* dvg = reinterpret_cast<bf16*>(p.dv) + slice * DV;
+  if (wc0 < Nk) {
+    bf16* dkg = reinterpret_cast<bf16*>(p.dk) + kslice * D;
+    bf16* dvg = reinterpret_cast<bf16*>(p.dv) + kslice * DV;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = wc0 + 8 * (r / 4) + 4 * hh + (r % 4);
-      if (key < N) {
+      if (key < Nk) {
 #pragma unroll
         for (int mb = 0; mb < C::DO / 32; ++mb)
           dkg[(long long)key * D + col0 + 32 * mb + l32] = (bf16)(dkacc[mb][r] * p.scale);
@@ -499,32 +502,32 @@ __global__ __launch_bounds__(256, 1) void bwd_f32_kernel(BwdParams p) {
   const int kb = (int)(blockIdx.x / BH);
   const int b = bh / p.H, h = bh % p.H;
   const int hmi = p.hm == 1 ? 0 : h;
-  const int N = p.N;
-  const long long slice = (long long)bh * N;
-  const int c0 = kb * BKC, c1 = min(N, c0 + BKC);
+  const int Nq = p.Nq, Nk = p.Nk;
+  const long long qslice = (long long)bh * Nq, kslice = (long long)bh * Nk;
+  const int c0 = kb * BKC, c1 = min(Nk, c0 + BKC);
   const int wc0 = c0 + KW * w;
   const int j = wc0 + l32;
-  const float* qg = reinterpret_cast<const float*>(p.q) + slice * D;
-  const float* kg = reinterpret_cast<const float*>(p.k) + slice * D;
-  const float* vg = reinterpret_cast<const float*>(p.v) + slice * D;
-  const float* dog = reinterpret_cast<const float*>(p.dout) + slice * D;
+  const float* qg = reinterpret_cast<const float*>(p.q) + qslice * D;
+  const float* kg = reinterpret_cast<const float*>(p.k) + kslice * D;
+  const float* vg = reinterpret_cast<const float*>(p.v) + kslice * D;
+  const float* dog = reinterpret_cast<const float*>(p.dout) + qslice * D;
 
   for (int t = tid; t < BKC * D; t += 256) {
     const int row = t / D, col = t % D;
-    ks[row * S1 + col] = c0 + row < N ? kg[(long long)(c0 + row) * D + col] : 0.f;
+    ks[row * S1 + col] = c0 + row < Nk ? kg[(long long)(c0 + row) * D + col] : 0.f;
   }
   float kr[D / 2], vr[D / 2];
 #pragma unroll
   for (int t = 0; t < D / 2; ++t) {
-    kr[t] = j < N ? kg[(long long)j * D + 2 * t + hh] : 0.f;
-    vr[t] = j < N ? vg[(long long)j * D + 2 * t + hh] : 0.f;
+    kr[t] = j < Nk ? kg[(long long)j * D + 2 * t + hh] : 0.f;
+    vr[t] = j < Nk ? vg[(long long)j * D + 2 * t + hh] : 0.f;
   }
-  const long long vrow = ((long long)b * p.hm + hmi) * N;
-  int k_lts = N, k_lte = N, k_uts = 0, k_ute = 0;
-  if (j < N) {
+  const long long vrow = ((long long)b * p.hm + hmi) * Nk;
+  int k_lts = Nq, k_lte = Nq, k_uts = 0, k_ute = 0;   // empty intervals
+  if (j < Nk) {
     if (p.has_lt) {
       k_lts = p.lts[vrow + j];
-      k_lte = p.has_lte ? p.lte[vrow + j] : N;
+      k_lte = p.has_lte ? p.lte[vrow + j] : Nq;
     }
     if (p.has_ut) {
       k_uts = p.uts[vrow + j];
@@ -546,32 +549,32 @@ __global__ __launch_bounds__(256, 1) void bwd_f32_kernel(BwdParams p) {
     kbnd.uts_mn = min(kbnd.uts_mn, q.uts_mn); kbnd.uts_mx = max(kbnd.uts_mx, q.uts_mx);
     kbnd.ute_mn = min(kbnd.ute_mn, q.ute_mn); kbnd.ute_mx = max(kbnd.ute_mx, q.ute_mx);
   }
-  const BlockBounds wbnd = load_bounds(table + (long long)(min(wc0, N - 1) / 64) * 8);
+  const BlockBounds wbnd = load_bounds(table + (long long)(min(wc0, Nk - 1) / 64) * 8);
   unsigned cnt0 = 0, cnt1 = 0, cnt2 = 0;
 
   for (int qb = 0; qb < p.nqb; ++qb) {
-    const int q0 = qb * BQ, q1 = min(N, q0 + BQ);
+    const int q0 = qb * BQ, q1 = min(Nq, q0 + BQ);
     const int wgc = tile_class(kbnd, q0, q1, c0, c1, p.causal != 0);
     cnt0 += wgc == 0;
     cnt1 += wgc == 1;
     cnt2 += wgc == 2;
     if (wgc == 0) continue;
     int wc = 0;
-    if (wc0 < N) {
-      wc = tile_class(wbnd, q0, q1, wc0, min(N, wc0 + KW), p.causal != 0);
+    if (wc0 < Nk) {
+      wc = tile_class(wbnd, q0, q1, wc0, min(Nk, wc0 + KW), p.causal != 0);
       if (wc == 2 && (q1 - q0 < BQ || c1 - c0 < BKC)) wc = 1;
     }
     __syncthreads();  // previous step's readers are done
     for (int t = tid; t < BQ * D; t += 256) {
       const int row = t / D, col = t % D;
-      const bool ok = q0 + row < N;
+      const bool ok = q0 + row < Nq;
       qs[row * S1 + col] = ok ? qg[(long long)(q0 + row) * D + col] : 0.f;
       dos[row * S1 + col] = ok ? dog[(long long)(q0 + row) * D + col] : 0.f;
     }
     if (tid < BQ) {
-      const bool ok = q0 + tid < N;
-      lse_s[tid] = ok ? p.lse2[slice + q0 + tid] : __builtin_inff();
-      del_s[tid] = ok ? p.delta[slice + q0 + tid] : 0.f;
+      const bool ok = q0 + tid < Nq;
+      lse_s[tid] = ok ? p.lse2[qslice + q0 + tid] : __builtin_inff();
+      del_s[tid] = ok ? p.delta[qslice + q0 + tid] : 0.f;
     }
     __syncthreads();
     f32x16 pr = f32x16{}, dsr = f32x16{};
@@ -588,7 +591,7 @@ __global__ __launch_bounds__(256, 1) void bwd_f32_kernel(BwdParams p) {
         const int i = q0 + il;
         float sv = sacc[r];
         if (wc == 1) {
-          bool m = (i >= N) || (j >= N) || (p.causal && j > i);
+          bool m = (i >= Nq) || (j >= Nk) || (p.causal && j > i);
           m = m || (k_lts <= i && i < k_lte) || (k_uts <= i && i < k_ute);
           if (m) sv = kNegInf;
         }
@@ -618,19 +621,19 @@ __global__ __launch_bounds__(256, 1) void bwd_f32_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = q0 + 8 * (r / 4) + 4 * hh + (r % 4);
-        if (i < N) unsafeAtomicAdd(p.dq_acc + (slice + i) * D + 32 * mb + l32, dq[r]);
+        if (i < Nq) unsafeAtomicAdd(p.dq_acc + (qslice + i) * D + 32 * mb + l32, dq[r]);
       }
     }
   }
-  if (wc0 < N) {
-    float* dkg = reinterpret_cast<float*>(p.dk) + slice * D;
-    float* dvg = reinterpret_cast<float*>(p.dv) + slice * D;
+  if (wc0 < Nk) {
+    float* dkg = reinterpret_cast<float*>(p.dk) + kslice * D;
+    float* dvg = reinterpret_cast<float*>(p.dv) + kslice * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = wc0 + 8 * (r / 4) + 4 * hh + (r % 4);
-        if (key < N) {
+        if (key < Nk) {
           dkg[(long long)key * D + 32 * mb + l32] = dkacc[mb][r];
           dvg[(long long)key * D + 32 * mb + l32] = dvacc[mb][r];
         }
@@ -646,7 +649,7 @@ __global__ __launch_bounds__(256, 1) void bwd_f32_kernel(BwdParams p) {
 // ---------------------------------------------------------------- launch
 template <int D, typename T>
 static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
-  const long long rows = (long long)p.B * p.H * p.N;
+  const long long rows = (long long)p.B * p.H * p.Nq;
   const long long blocks = (rows + 15) / 16;
   hipLaunchKernelGGL((bwd_pre_kernel<D, T>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -654,7 +657,7 @@ static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
 
 template <typename T>
 static hipError_t launch_convert(const BwdParams& p, int d, hipStream_t stream) {
-  const long long n4 = (long long)p.B * p.H * p.N * d / 4;
+  const long long n4 = (long long)p.B * p.H * p.Nq * d / 4;
   long long blocks = (n4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL((dq_convert_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, stream, p.dq_acc,
@@ -665,7 +668,7 @@ static hipError_t launch_convert(const BwdParams& p, int d, hipStream_t stream) 
 template <int D, int DV>
 static hipError_t launch_bwd_bf16(BwdParams p, const AttnArgs& a, hipStream_t stream) {
   using C = BwdCfg<D, DV>;
-  p.nqb = (p.N + C::BQ - 1) / C::BQ;
+  p.nqb = (p.Nq + C::BQ - 1) / C::BQ;
   // the dQ pass also writes delta and the base-2 LSE the dK/dV pass reads
   const hipError_t e = launch_bwd_dq(a, stream);
   if (e != hipSuccess) return e;
@@ -676,7 +679,7 @@ static hipError_t launch_bwd_bf16(BwdParams p, const AttnArgs& a, hipStream_t st
 
 template <int D>
 static hipError_t launch_bwd_f32(BwdParams p, hipStream_t stream) {
-  p.nqb = (p.N + 31) / 32;
+  p.nqb = (p.Nq + 31) / 32;
   hipError_t e = launch_pre<D, float>(p, stream);
   if (e != hipSuccess) return e;
   const long long grid = (long long)p.B * p.H * p.nkb;
@@ -686,7 +689,32 @@ static hipError_t launch_bwd_f32(BwdParams p, hipStream_t stream) {
   return launch_convert<float>(p, D, stream);
 }
 
+// ---------------------------------------------------------------- zero fill
+// Gradients of a side with no partner (no keys, or no query rows) are zero.
+__global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ p, long long n16) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (long long)gridDim.x * blockDim.x)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+static hipError_t launch_zero(void* p, long long bytes, hipStream_t stream) {
+  const long long n16 = bytes / 16;   // row sizes are multiples of 16 bytes
+  if (n16 == 0) return hipSuccess;
+  long long blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<u32x4*>(p), n16);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
+  const long long elt = a.is_bf16 ? 2 : 4;
+  if (a.Nk == 0) return launch_zero(a.dq, (long long)a.B * a.H * a.Nq * a.d * elt, stream);
+  if (a.Nq == 0) {
+    const hipError_t e = launch_zero(a.dk, (long long)a.B * a.H * a.Nk * a.d * elt, stream);
+    if (e != hipSuccess) return e;
+    return launch_zero(a.dv_out, (long long)a.B * a.H * a.Nk * a.dv * elt, stream);
+  }
   BwdParams p{};
   p.q = a.q;
   p.k = a.k;
@@ -708,7 +736,8 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.counts = a.tile_counts;
   p.B = a.B;
   p.H = a.H;
-  p.N = a.N;
+  p.Nq = a.Nq;
+  p.Nk = a.Nk;
   p.hm = a.mask.hm;
   p.causal = a.mask.causal;
   p.has_lt = a.mask.lts != nullptr;
@@ -716,8 +745,8 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   p.has_ut = !a.mask.causal && a.mask.uts != nullptr && a.mask.ute != nullptr;
   p.scale = a.scale;
   p.sl2 = a.scale * kLog2e;
-  p.nkb = (a.N + kBwdBlockK - 1) / kBwdBlockK;
-  p.nkb64 = (a.N + kTableBlock - 1) / kTableBlock;
+  p.nkb = (a.Nk + kBwdBlockK - 1) / kBwdBlockK;
+  p.nkb64 = (a.Nk + kTableBlock - 1) / kTableBlock;
   if (a.is_bf16) {
     // the bf16 (d, dv) pairs compiled in (kept in step with bf16_dims())
     if (a.d == 64 && a.dv == 64) return launch_bwd_bf16<64, 64>(p, a, stream);

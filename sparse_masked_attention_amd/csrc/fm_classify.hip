@@ -15,8 +15,9 @@ namespace fm {
 
 // One wave per (batch * mask head, key block): lanes stride over the block's
 // columns, then a butterfly over the wave reduces the eight running values.
-__global__ __launch_bounds__(256) void kblock_minmax_kernel(MaskArgs m, int BHm, int N, int block,
-                                                            int nkb, int32_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void kblock_minmax_kernel(MaskArgs m, int BHm, int Nq, int N,
+                                                            int block, int nkb,
+                                                            int32_t* __restrict__ out) {
   const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (wave >= (long long)BHm * nkb) return;  // whole waves leave together
@@ -31,8 +32,9 @@ __global__ __launch_bounds__(256) void kblock_minmax_kernel(MaskArgs m, int BHm,
   int mx[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
   for (long long c = c0 + lane; c < c1; c += 64) {
     int v[4];
-    v[0] = has_lt ? m.lts[base + c] : N;
-    v[1] = (has_lt && m.lte != nullptr) ? m.lte[base + c] : N;
+    // N key columns; a missing lower interval is [Nq, Nq) (Nq query rows)
+    v[0] = has_lt ? m.lts[base + c] : Nq;
+    v[1] = (has_lt && m.lte != nullptr) ? m.lte[base + c] : Nq;
     v[2] = has_ut ? m.uts[base + c] : 0;
     v[3] = has_ut ? m.ute[base + c] : 0;
 #pragma unroll
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(256) void kblock_minmax_kernel(MaskArgs m, int BHm,
 }
 
 __global__ __launch_bounds__(256) void classify_kernel(const int32_t* __restrict__ table, long long total,
-                                                       int N, int bq, int bk, int nqb, int nkb,
+                                                       int Nq, int Nk, int bq, int bk, int nqb, int nkb,
                                                        int causal, int8_t* __restrict__ out) {
   for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (long long)gridDim.x * blockDim.x) {
@@ -72,33 +74,33 @@ __global__ __launch_bounds__(256) void classify_kernel(const int32_t* __restrict
     const long long bhm = rest / nqb;
     const long long r0 = (long long)qb * bq;
     const long long c0 = (long long)kb * bk;
-    const int r1 = (int)(r0 + bq < N ? r0 + bq : N);
-    const int c1 = (int)(c0 + bk < N ? c0 + bk : N);
+    const int r1 = (int)(r0 + bq < Nq ? r0 + bq : Nq);
+    const int c1 = (int)(c0 + bk < Nk ? c0 + bk : Nk);
     const BlockBounds t = load_bounds(table + (bhm * nkb + kb) * 8);
     out[idx] = (int8_t)tile_class(t, (int)r0, r1, (int)c0, c1, causal != 0);
   }
 }
 
-hipError_t launch_kblock_minmax(const MaskArgs& m, int B, int N, int block, int32_t* out,
+hipError_t launch_kblock_minmax(const MaskArgs& m, int B, int Nq, int N, int block, int32_t* out,
                                 hipStream_t stream) {
   const int nkb = (int)(((long long)N + block - 1) / block);
   const long long waves = (long long)B * m.hm * nkb;
   const long long blocks = (waves + 3) / 4;
   if (blocks > INT_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kblock_minmax_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, m, B * m.hm,
-                     N, block, nkb, out);
+                     Nq, N, block, nkb, out);
   return hipGetLastError();
 }
 
-hipError_t launch_classify(const int32_t* table, int B, int hm, int N, int causal, int block_q,
-                           int block_k, int8_t* out, hipStream_t stream) {
-  const int nqb = (int)(((long long)N + block_q - 1) / block_q);
-  const int nkb = (int)(((long long)N + block_k - 1) / block_k);
+hipError_t launch_classify(const int32_t* table, int B, int hm, int Nq, int Nk, int causal,
+                           int block_q, int block_k, int8_t* out, hipStream_t stream) {
+  const int nqb = (int)(((long long)Nq + block_q - 1) / block_q);
+  const int nkb = (int)(((long long)Nk + block_k - 1) / block_k);
   const long long total = (long long)B * hm * nqb * nkb;
   long long blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(classify_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, table, total, N,
-                     block_q, block_k, nqb, nkb, causal, out);
+  hipLaunchKernelGGL(classify_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, table, total, Nq,
+                     Nk, block_q, block_k, nqb, nkb, causal, out);
   return hipGetLastError();
 }
 

@@ -49,7 +49,7 @@ struct FwdParams {
   float* lse2;
   float* delta;
   void* dq;
-  int B, H, N, hm, causal;
+  int B, H, Nq, Nk, hm, causal;   // Nq query rows, Nk keys
   int has_lt, has_lte, has_ut;
   float scale, sl2;
   int nqb, nkb;
@@ -73,8 +73,8 @@ __device__ inline void mask_block(f32x16& s, const FM_LDS int* vl, int kl0, int 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int j = kbase + kl + e;
-      bool m = (j >= p.N) || (p.causal && j > i);
-      const int lte_v = p.has_lte ? lte4[e] : p.N;
+      bool m = (j >= p.Nk) || (p.causal && j > i);
+      const int lte_v = p.has_lte ? lte4[e] : p.Nq;
       m = m || (p.has_lt && lts4[e] <= i && i < lte_v);
       m = m || (p.has_ut && uts4[e] <= i && i < ute4[e]);
       if (m) s[4 * g + e] = kNegInf;
@@ -159,28 +159,31 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
   qb = p.nqb - 1 - qb;                                   // heavy (late) query blocks first
   const int b = bh / p.H, h = bh % p.H;
   const int hmi = p.hm == 1 ? 0 : h;
-  const int N = p.N;
-  const long long slice = (long long)bh * N;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const long long qslice = (long long)bh * Nq;           // rows of Q, O, dO, LSE
+  const long long kslice = (long long)bh * Nk;           // rows of K, V
   const int r0 = qb * C::BR;
-  const int r1 = min(N, r0 + C::BR);
+  const int r1 = min(Nq, r0 + C::BR);
   const int wr0 = r0 + C::WR * w;                       // this wave's first row
   const int i = wr0 + l32;                              // this lane's row
-  const uint32_t tbytes = (uint32_t)N * D * 2;     // one head of Q or K
-  const uint32_t vbytes = (uint32_t)N * DV * 2;    // one head of V, O or dO
+  const uint32_t qbytes = (uint32_t)Nq * D * 2;    // one head of Q
+  const uint32_t kbytes = (uint32_t)Nk * D * 2;    // one head of K
+  const uint32_t vbytes = (uint32_t)Nk * DV * 2;   // one head of V
+  const uint32_t obytes = (uint32_t)Nq * DV * 2;   // one head of O or dO
 
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(p.q) + slice * D, tbytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + slice * D, tbytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + slice * DV, vbytes);
-  const long long vrow = ((long long)b * p.hm + hmi) * N;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(p.q) + qslice * D, qbytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + kslice * D, kbytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + kslice * DV, vbytes);
+  const long long vrow = ((long long)b * p.hm + hmi) * Nk;
   const int32_t* vecs[4] = {p.lts, p.lte, p.uts, p.ute};
   // each wave stages one of the four boundary vectors (absent ones read as 0)
   const int32_t* my_vec = vecs[w & 3];
   const bool vec_present = my_vec != nullptr && (w < 2 ? p.has_lt : p.has_ut);
   const __amdgpu_buffer_rsrc_t rvec =
-      make_rsrc(vec_present ? my_vec + vrow : p.table, vec_present ? (uint32_t)N * 4 : 0u);
+      make_rsrc(vec_present ? my_vec + vrow : p.table, vec_present ? (uint32_t)Nk * 4 : 0u);
 
   // This lane's row of Q (and dO) as B operands: chunk c holds
-  // [i][16c + 8h .. +7]. Rows past N read as zero.
+  // [i][16c + 8h .. +7]. Rows past Nq read as zero.
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c)
@@ -189,13 +192,13 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
   float row_lse2 = 0.f, row_delta = 0.f;
   if constexpr (DQ) {
     const __amdgpu_buffer_rsrc_t rdo =
-        make_rsrc(reinterpret_cast<const bf16*>(p.dout) + slice * DV, vbytes);
+        make_rsrc(reinterpret_cast<const bf16*>(p.dout) + qslice * DV, obytes);
 #pragma unroll
     for (int c = 0; c < DV / 16; ++c)
       dof[c] = __builtin_bit_cast(bf16x8, buffer_load16(rdo, (uint32_t)(i * DV + 16 * c + 8 * hh) * 2));
     // delta_i = dO_i . O_i: this lane holds half of row i (the chunks of
     // its half-wave), the other half-wave the rest
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<const bf16*>(p.o_in) + slice * DV, vbytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<const bf16*>(p.o_in) + qslice * DV, obytes);
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     float dl = 0.f;
 #pragma unroll
@@ -207,11 +210,11 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
     }
     row_delta = sum_x32(dl);
     // base-2 LSE; a fully masked row (LSE -inf) gets +inf, so its P is 0
-    const float l = i < N ? p.lse_in[slice + i] : kNegInf;
+    const float l = i < Nq ? p.lse_in[qslice + i] : kNegInf;
     row_lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
-    if (hh == 0 && i < N) {
-      p.delta[slice + i] = row_delta;
-      p.lse2[slice + i] = row_lse2;
+    if (hh == 0 && i < Nq) {
+      p.delta[qslice + i] = row_delta;
+      p.lse2[qslice + i] = row_lse2;
     }
   }
 
@@ -283,8 +286,8 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
     if (wc == 1) {
       // one key per lane: which of this wave's 32 rows the mask hides for it
       // (absent vectors were staged as zeros, and has_* gates their use)
-      mwords[w][lane] = key_row_mask(kbase + lane, wr0, N, causal, has_lt, has_ut, vl[lane],
-                                     has_lte ? vl[64 + lane] : N, vl[128 + lane], vl[192 + lane]);
+      mwords[w][lane] = key_row_mask(kbase + lane, wr0, Nk, causal, has_lt, has_ut, vl[lane],
+                                     has_lte ? vl[64 + lane] : Nq, vl[128 + lane], vl[192 + lane]);
       __builtin_amdgcn_wave_barrier();
     }
     // S^T starts at the mask's additive bias (-inf where masked, else 0): the
@@ -388,7 +391,7 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
     bool valid = false;
     if (kb < p.nkb) {
       const BlockBounds bb = load_bounds(table + (long long)kb * 8);
-      const int c0 = kb * C::BC, c1 = min(N, c0 + C::BC);
+      const int c0 = kb * C::BC, c1 = min(Nk, c0 + C::BC);
       const int wgc = tile_class(bb, r0, r1, c0, c1, causal);
       cnt0 += wgc == 0;
       cnt1 += wgc == 1;
@@ -400,8 +403,8 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
         for (int ww = 0; ww < C::NW; ++ww) {
           const int a0 = r0 + C::WR * ww;
           int cl = 0;
-          if (a0 < N) {
-            cl = tile_class(bb, a0, min(N, a0 + C::WR), c0, c1, causal);
+          if (a0 < Nq) {
+            cl = tile_class(bb, a0, min(Nq, a0 + C::WR), c0, c1, causal);
             if (ragged && cl == 2) cl = 1;
           }
           bits |= (unsigned)cl << (2 * ww);
@@ -458,8 +461,8 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
     // normalise, store O (bf16) and the natural-log LSE
     const float lt = sum_x32(l_run);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (i < N) {
-      bf16* og = reinterpret_cast<bf16*>(p.o) + (slice + i) * DV;
+    if (i < Nq) {
+      bf16* og = reinterpret_cast<bf16*>(p.o) + (qslice + i) * DV;
 #pragma unroll
       for (int mb = 0; mb < DV / 32; ++mb)
 #pragma unroll
@@ -469,12 +472,12 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
           for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[mb][4 * g + e] * inv);
           *reinterpret_cast<bf16x4*>(og + 32 * mb + 8 * g + 4 * hh) = v4;
         }
-      if (hh == 0) p.lse[slice + i] = lt > 0.f ? m_run * p.scale + __logf(lt) : kNegInf;
+      if (hh == 0) p.lse[qslice + i] = lt > 0.f ? m_run * p.scale + __logf(lt) : kNegInf;
     }
   } else {
     // dQ = scale * dS K
-    if (i < N) {
-      bf16* dqg = reinterpret_cast<bf16*>(p.dq) + (slice + i) * D;
+    if (i < Nq) {
+      bf16* dqg = reinterpret_cast<bf16*>(p.dq) + (qslice + i) * D;
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
@@ -514,19 +517,19 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
   const int qb = p.nqb - 1 - (int)(blockIdx.x / BH);
   const int b = bh / p.H, h = bh % p.H;
   const int hmi = p.hm == 1 ? 0 : h;
-  const int N = p.N;
-  const long long slice = (long long)bh * N;
-  const int r0 = qb * BR, r1 = min(N, r0 + BR);
+  const int Nq = p.Nq, Nk = p.Nk;
+  const long long qslice = (long long)bh * Nq, kslice = (long long)bh * Nk;
+  const int r0 = qb * BR, r1 = min(Nq, r0 + BR);
   const int i = r0 + 32 * w + (lane & 31);
-  const float* qg = reinterpret_cast<const float*>(p.q) + slice * D;
-  const float* kg = reinterpret_cast<const float*>(p.k) + slice * D;
-  const float* vg = reinterpret_cast<const float*>(p.v) + slice * D;
-  const long long vrow = ((long long)b * p.hm + hmi) * N;
+  const float* qg = reinterpret_cast<const float*>(p.q) + qslice * D;
+  const float* kg = reinterpret_cast<const float*>(p.k) + kslice * D;
+  const float* vg = reinterpret_cast<const float*>(p.v) + kslice * D;
+  const long long vrow = ((long long)b * p.hm + hmi) * Nk;
   const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb * 8;
 
   float qf[D / 2];
 #pragma unroll
-  for (int t = 0; t < D / 2; ++t) qf[t] = i < N ? qg[(long long)i * D + 2 * t + hh] : 0.f;
+  for (int t = 0; t < D / 2; ++t) qf[t] = i < Nq ? qg[(long long)i * D + 2 * t + hh] : 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16{};
@@ -535,7 +538,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
 
   for (int kb = 0; kb < p.nkb; ++kb) {
     const BlockBounds bb = load_bounds(table + (long long)kb * 8);
-    const int c0 = kb * BC, c1 = min(N, c0 + BC);
+    const int c0 = kb * BC, c1 = min(Nk, c0 + BC);
     const int wgc = tile_class(bb, r0, r1, c0, c1, p.causal != 0);
     cnt0 += wgc == 0;
     cnt1 += wgc == 1;
@@ -543,14 +546,14 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
     if (wgc == 0) continue;
     int wc = 0;
     const int a0 = r0 + 32 * w;
-    if (a0 < N) {
-      wc = tile_class(bb, a0, min(N, a0 + 32), c0, c1, p.causal != 0);
+    if (a0 < Nq) {
+      wc = tile_class(bb, a0, min(Nq, a0 + 32), c0, c1, p.causal != 0);
       if (c1 - c0 < BC && wc == 2) wc = 1;
     }
     __syncthreads();
     for (int t = tid; t < BC * D; t += 256) {
       const int row = t / D, col = t % D;
-      const bool ok = c0 + row < N;
+      const bool ok = c0 + row < Nk;
       ks[row * KS + col] = ok ? kg[(long long)(c0 + row) * D + col] : 0.f;
       vs[row * VS + col] = ok ? vg[(long long)(c0 + row) * D + col] : 0.f;
     }
@@ -558,7 +561,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
       const int vsel = tid >> 6, kk = tid & 63;
       const int32_t* src = vsel == 0 ? p.lts : vsel == 1 ? p.lte : vsel == 2 ? p.uts : p.ute;
       const bool present = src != nullptr && (vsel < 2 ? p.has_lt : p.has_ut);
-      vl[vsel * 64 + kk] = (present && c0 + kk < N) ? src[vrow + c0 + kk] : 0;
+      vl[vsel * 64 + kk] = (present && c0 + kk < Nk) ? src[vrow + c0 + kk] : 0;
     }
     __syncthreads();
     if (wc == 0) continue;
@@ -605,8 +608,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
 
   const float lt = sum_x32(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (i < N) {
-    float* og = reinterpret_cast<float*>(p.o) + (slice + i) * D;
+  if (i < Nq) {
+    float* og = reinterpret_cast<float*>(p.o) + (qslice + i) * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)
 #pragma unroll
@@ -616,7 +619,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
         for (int e = 0; e < 4; ++e) v4[e] = oacc[mb][4 * g + e] * inv;
         *reinterpret_cast<f32x4*>(og + 32 * mb + 8 * g + 4 * hh) = v4;
       }
-    if (hh == 0) p.lse[slice + i] = lt > 0.f ? m_run * p.scale + logf(lt) : kNegInf;
+    if (hh == 0) p.lse[qslice + i] = lt > 0.f ? m_run * p.scale + logf(lt) : kNegInf;
   }
   if (p.counts != nullptr && tid == 0) {
     atomicAdd(p.counts + 0, (unsigned long long)cnt0);
@@ -629,7 +632,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
 template <int D, int DV, int MODE>
 static hipError_t launch_qmajor(FwdParams p, hipStream_t stream) {
   using C = QCfg<D, DV, MODE>;
-  p.nqb = (p.N + C::BR - 1) / C::BR;
+  p.nqb = (p.Nq + C::BR - 1) / C::BR;
   const long long grid = (long long)p.B * p.H * p.nqb;
   hipLaunchKernelGGL((qmajor_bf16_kernel<D, DV, MODE>), dim3((unsigned)grid), dim3(C::NW * 64), 0, stream, p);
   return hipGetLastError();
@@ -647,7 +650,7 @@ static hipError_t dispatch_qmajor(int d, int dv, const FwdParams& p, hipStream_t
 
 template <int D>
 static hipError_t launch_fwd_f32(FwdParams p, hipStream_t stream) {
-  p.nqb = (p.N + 127) / 128;
+  p.nqb = (p.Nq + 127) / 128;
   const long long grid = (long long)p.B * p.H * p.nqb;
   hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -668,7 +671,8 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
   p.counts = a.tile_counts;
   p.B = a.B;
   p.H = a.H;
-  p.N = a.N;
+  p.Nq = a.Nq;
+  p.Nk = a.Nk;
   p.hm = a.mask.hm;
   p.causal = a.mask.causal;
   p.has_lt = a.mask.lts != nullptr;
@@ -676,7 +680,7 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
   p.has_ut = !a.mask.causal && a.mask.uts != nullptr && a.mask.ute != nullptr;
   p.scale = a.scale;
   p.sl2 = a.scale * kLog2e;
-  p.nkb = (a.N + kFwdBlockK - 1) / kFwdBlockK;
+  p.nkb = (a.Nk + kFwdBlockK - 1) / kFwdBlockK;
   if (a.is_bf16) {
     return dispatch_qmajor<kModeFwd>(a.d, a.dv, p, stream);
   } else {
@@ -711,7 +715,8 @@ hipError_t launch_bwd_dq(const AttnArgs& a, hipStream_t stream) {
   p.dq = a.dq;
   p.B = a.B;
   p.H = a.H;
-  p.N = a.N;
+  p.Nq = a.Nq;
+  p.Nk = a.Nk;
   p.hm = a.mask.hm;
   p.causal = a.mask.causal;
   p.has_lt = a.mask.lts != nullptr;
@@ -719,7 +724,7 @@ hipError_t launch_bwd_dq(const AttnArgs& a, hipStream_t stream) {
   p.has_ut = !a.mask.causal && a.mask.uts != nullptr && a.mask.ute != nullptr;
   p.scale = a.scale;
   p.sl2 = a.scale * kLog2e;
-  p.nkb = (a.N + kFwdBlockK - 1) / kFwdBlockK;
+  p.nkb = (a.Nk + kFwdBlockK - 1) / kFwdBlockK;
   return dispatch_qmajor<kModeDq>(a.d, a.dv, p, stream);
 }
 

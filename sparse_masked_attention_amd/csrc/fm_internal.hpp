@@ -25,7 +25,7 @@ inline bool bf16_dims(int d, int dv) {
 inline bool fp32_dims(int d, int dv) { return d == dv && (d == 64 || d == 128); }
 
 struct MaskArgs {
-  const int32_t* lts;  // [B, hm, N] or nullptr
+  const int32_t* lts;  // [B, hm, Nk] or nullptr
   const int32_t* lte;
   const int32_t* uts;
   const int32_t* ute;
@@ -42,7 +42,7 @@ struct AttnArgs {
   const void* dout;   // backward input
   MaskArgs mask;
   const int32_t* table;  // [B, hm, ceil(N / kTableBlock), 8]
-  int B, H, N, d, dv;
+  int B, H, Nq, Nk, d, dv;   // Nq query rows, Nk keys
   int is_bf16;
   float scale;
   void* out;          // forward: O
@@ -56,10 +56,16 @@ struct AttnArgs {
   unsigned long long* tile_counts;
 };
 
-hipError_t launch_kblock_minmax(const MaskArgs& m, int B, int N, int block, int32_t* out,
+// table over Nk key columns; missing vectors take the neutral bounds of Nq rows
+hipError_t launch_kblock_minmax(const MaskArgs& m, int B, int Nq, int Nk, int block, int32_t* out,
                                 hipStream_t stream);
-hipError_t launch_classify(const int32_t* table, int B, int hm, int N, int causal, int block_q,
-                           int block_k, int8_t* out, hipStream_t stream);
+hipError_t launch_classify(const int32_t* table, int B, int hm, int Nq, int Nk, int causal,
+                           int block_q, int block_k, int8_t* out, hipStream_t stream);
+// at most this many query-row chunks per rank in flashmask_localize
+constexpr int kMaxChunks = 64;
+hipError_t launch_localize(const MaskArgs& m, int B, int Nk, int n_rows, const int32_t* chunks,
+                           int nchunks, int32_t* lts_o, int32_t* lte_o, int32_t* uts_o,
+                           int32_t* ute_o, hipStream_t stream);
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, hipStream_t stream);

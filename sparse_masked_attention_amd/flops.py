@@ -16,8 +16,10 @@ import numpy as np
 __all__ = ["nnz_columns", "nnz", "fwd_flops", "bwd_flops"]
 
 
-def nnz_columns(n, causal, lts=None, lte=None, uts=None, ute=None) -> np.ndarray:
-    """Open pairs per column for one (batch, head); vectors are [N] or None."""
+def nnz_columns(n, causal, lts=None, lte=None, uts=None, ute=None, n_rows=None) -> np.ndarray:
+    """Open pairs per column for one (batch, head); n key columns, vectors
+    [n] or None, n_rows query rows (default n)."""
+    nr = n if n_rows is None else int(n_rows)
     j = np.arange(n, dtype=np.int64)
     zero = np.zeros(n, np.int64)
     starts, ends = [], []
@@ -25,16 +27,16 @@ def nnz_columns(n, causal, lts=None, lte=None, uts=None, ute=None) -> np.ndarray
         starts.append(zero)
         ends.append(j)
     if lts is not None:
-        e = np.full(n, n, np.int64) if lte is None else np.asarray(lte, np.int64)
+        e = np.full(n, nr, np.int64) if lte is None else np.asarray(lte, np.int64)
         starts.append(np.asarray(lts, np.int64))
         ends.append(e)
     if (not causal) and uts is not None and ute is not None:
         starts.append(np.asarray(uts, np.int64))
         ends.append(np.asarray(ute, np.int64))
     if not starts:
-        return np.full(n, n, np.int64)
-    s = np.clip(np.stack(starts), 0, n)
-    e = np.clip(np.stack(ends), 0, n)
+        return np.full(n, nr, np.int64)
+    s = np.clip(np.stack(starts), 0, nr)
+    e = np.clip(np.stack(ends), 0, nr)
     e = np.maximum(s, e)                       # empty interval -> zero length
     order = np.argsort(s, axis=0, kind="stable")
     s = np.take_along_axis(s, order, axis=0)
@@ -45,11 +47,12 @@ def nnz_columns(n, causal, lts=None, lte=None, uts=None, ute=None) -> np.ndarray
         lo = np.maximum(s[t], reach)
         covered += np.maximum(0, e[t] - lo)
         reach = np.maximum(reach, e[t])
-    return n - covered
+    return nr - covered
 
 
-def nnz(B, H, n, causal, lts=None, lte=None, uts=None, ute=None) -> int:
-    """Open pairs summed over all (batch, head); vectors are [B, Hm, N] or None."""
+def nnz(B, H, n, causal, lts=None, lte=None, uts=None, ute=None, n_rows=None) -> int:
+    """Open pairs summed over all (batch, head); vectors are [B, Hm, n] or None
+    over n keys, n_rows query rows (default n)."""
     def row(v, b, h):
         if v is None:
             return None
@@ -61,7 +64,7 @@ def nnz(B, H, n, causal, lts=None, lte=None, uts=None, ute=None) -> int:
     for b in range(B):
         for h in range(hm):
             c = int(nnz_columns(n, causal, row(lts, b, h), row(lte, b, h),
-                                row(uts, b, h), row(ute, b, h)).sum())
+                                row(uts, b, h), row(ute, b, h), n_rows=n_rows).sum())
             total += c * (H if hm == 1 else 1)
     return total
 

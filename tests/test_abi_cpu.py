@@ -30,7 +30,9 @@ def test_header_declares_the_abi():
     names = declared_symbols()
     for n in ["flashmask_tile_classify", "flashmask_fwd", "flashmask_bwd",
               "flashmask_workspace_size", "flashmask_status_string", "flashmask_table_block",
-              "flashmask_tile_shape"]:
+              "flashmask_tile_shape", "flashmask_tile_classify_qk", "flashmask_fwd_qk",
+              "flashmask_bwd_qk", "flashmask_workspace_size_qk", "flashmask_localize",
+              "flashmask_max_chunks"]:
         assert n in names
 
 
@@ -140,3 +142,44 @@ def test_binding_refuses_cpu_tensors(lib):
     m = _binding.Mask(None, None, None, None, True)
     with pytest.raises(ValueError):
         _binding.fwd(q, q, q, m)
+
+
+def test_rectangular_workspace_and_empty_sides(lib):
+    import torch
+    # table over Nk keys, delta and base-2 LSE over Nq rows
+    # 5 key blocks x 32 bytes -> 256; 2 x (1 x 2 x 100 floats) -> 2 x 1024
+    assert _binding.workspace_size(True, 1, 2, 100, 128, 128, 1, torch.bfloat16, Nk=300) == \
+        256 + 2 * 1024
+    assert _binding.workspace_size(False, 1, 2, 100, 128, 128, 1, torch.bfloat16, Nk=0) == 0
+    p = lambda x: None if x is None else ctypes.c_void_p(x * 256)
+    fwd = lambda Nq, Nk, q=1: lib.flashmask_fwd_qk(p(q), p(1), p(1), p(1), None, None, None, 1, None,
+                                                   1, 2, Nq, Nk, 128, 128, 1, 1, 0.0, p(1), p(1),
+                                                   None, p(1), 1 << 30, None)
+    assert fwd(0, 64, q=None) == FM_SUCCESS       # no query row: nothing to do
+    assert fwd(16, -1) == FM_INVALID
+    assert fwd(-1, 16) == FM_INVALID
+    bwd = lambda Nq, Nk: lib.flashmask_bwd_qk(p(1), p(1), p(1), p(1), p(1), p(1), p(1), None, None,
+                                              None, 1, None, 1, 2, Nq, Nk, 128, 128, 1, 1, 0.0,
+                                              p(1), p(1), p(1), None, p(1), 1 << 30, None)
+    assert bwd(0, 0) == FM_SUCCESS
+    assert bwd(-3, 5) == FM_INVALID
+
+
+def test_localize_argument_checks(lib):
+    assert lib.flashmask_max_chunks() == _binding.max_chunks() >= 8
+    p = lambda x: None if x is None else ctypes.c_void_p(x * 256)
+
+    def call(chunks, n_rows=100, Nk=16, causal=1, outs=1):
+        arr = (ctypes.c_int32 * max(1, len(chunks)))(*chunks) if chunks else None
+        n = len(chunks) // 2
+        return lib.flashmask_localize(p(1), None, None, None, 1, 1, Nk, n_rows, causal, arr, n,
+                                      p(outs), p(outs), p(outs), p(outs), None)
+    assert call([]) == FM_INVALID                       # no chunk
+    assert call([10, 5]) == FM_INVALID                  # empty range
+    assert call([0, 10, 5, 20]) == FM_INVALID           # overlapping
+    assert call([20, 30, 0, 10]) == FM_INVALID          # not sorted
+    assert call([0, 101]) == FM_INVALID                 # past the last row
+    assert call([-1, 4]) == FM_INVALID
+    assert call(list(range(0, 2 * 65 * 1, 1)), n_rows=1000) == FM_INVALID  # too many chunks
+    assert call([0, 10], Nk=0) == FM_SUCCESS            # no key column: nothing to write
+    assert call([0, 10], outs=None) == FM_INVALID

@@ -171,3 +171,17 @@ def test_missing_lte_means_every_local_row():
         np.testing.assert_array_equal(m[:, j], np.arange(nq) >= lts[j])
     tab = oracle.kblock_minmax(1, 1, nk, 4, lts[None, None], None, n_rows=nq)
     assert tab[0, 0, 0, 2] == nq and tab[0, 0, 0, 3] == nq
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_open_pair_count_rectangular(seed):
+    """The O(Nk) open-pair count with Nq rows equals the dense count."""
+    from sparse_masked_attention_amd import flops
+    rng = np.random.default_rng(300 + seed)
+    nq, nk = int(rng.integers(1, 120)), int(rng.integers(1, 120))
+    v = [rng.integers(-10, nq + 10, nk).astype(np.int32) for _ in range(4)]
+    for causal in (True, False):
+        for lte in (v[1], None):
+            dense = oracle.dense_mask(nk, causal, v[0], lte, v[2], v[3], n_rows=nq)
+            got = flops.nnz_columns(nk, causal, v[0], lte, v[2], v[3], n_rows=nq)
+            np.testing.assert_array_equal(got, (~dense).sum(axis=0))
