@@ -23,7 +23,13 @@ Readings of points the pages leave open:
     rows; uts/ute None (non-causal) -> no upper interval;
   * with Nq query rows and Nk keys (one context-parallel rank's share of the
     rows, FlashMask-3 abstract) the vectors have Nk entries and hold bounds
-    on the Nq local rows; the causal test stays j > i in local indices.
+    on the Nq local rows; the causal test stays j > i in local indices;
+  * sink bias (named in the README "News", not defined there): a per-head
+    logit s_h joins every row's softmax as one more, always open, entry with
+    a zero value vector, in the units of the scaled scores:
+    LSE_i = log(exp(s_h) + sum_open exp(S_ij)), P_ij = exp(S_ij - LSE_i),
+    O_i = sum_j P_ij V_j. A row with nothing open has O = 0 and LSE = s_h.
+    dL/ds_h = -sum_i exp(s_h - LSE_i) * (dO_i . O_i).
 
 Vectors are [B, Hm, N] with Hm in {1, H}; head h uses mask row h if Hm == H,
 else row 0.
@@ -75,26 +81,33 @@ def _scale(d: int, scale: Optional[float]) -> float:
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def softmax_probs(q: np.ndarray, k: np.ndarray, masked: np.ndarray, scale: float):
+def softmax_probs(q: np.ndarray, k: np.ndarray, masked: np.ndarray, scale: float,
+                  sink: Optional[float] = None):
     """Row-wise masked softmax of scale * q k^T for one (batch, head).
 
     q [R, d], k [N, d] in float64, masked [R, N]. Returns (P [R, N], lse [R]);
-    rows with every key masked get P = 0 and lse = -inf.
+    rows with every key masked get P = 0 and lse = -inf (lse = sink with a
+    sink logit, which takes part in every row's normaliser).
     """
     s = (q @ k.T) * scale
     s = np.where(masked, -np.inf, s)
-    empty = masked.all(axis=1)
+    if sink is not None:
+        # the sink as one more column, always open, with a zero value vector
+        s = np.concatenate([s, np.full((s.shape[0], 1), float(sink))], axis=1)
+    empty = np.isneginf(s).all(axis=1)
     m = np.where(empty, 0.0, s.max(axis=1))
     p = np.exp(s - m[:, None])          # exp(-inf) = 0 on masked entries
     l = p.sum(axis=1)
     l_safe = np.where(empty, 1.0, l)
     P = p / l_safe[:, None]
     lse = np.where(empty, -np.inf, m + np.log(l_safe))
+    if sink is not None:
+        P = P[:, :-1]                   # the sink's probability multiplies a zero value
     return P, lse
 
 
 def forward_rows(q, k, v, n, causal, lts=None, lte=None, uts=None, ute=None,
-                 rows=None, scale=None, chunk: int = 1024):
+                 rows=None, scale=None, chunk: int = 1024, sink: Optional[float] = None):
     """Forward of one (batch, head) for the given query rows.
 
     q [Nq, d], k [n, d], v [n, dv] (any float dtype, widened exactly to fp64);
@@ -113,18 +126,19 @@ def forward_rows(q, k, v, n, causal, lts=None, lte=None, uts=None, ute=None,
     for c0 in range(0, rows.shape[0], chunk):
         r = rows[c0:c0 + chunk]
         msk = dense_mask(n, causal, lts, lte, uts, ute, rows=r, n_rows=nq)
-        P, l = softmax_probs(q[r], k, msk, sc)
+        P, l = softmax_probs(q[r], k, msk, sc, sink)
         o[c0:c0 + chunk] = P @ v
         lse[c0:c0 + chunk] = l
     return o, lse
 
 
 def forward(q, k, v, causal, lts=None, lte=None, uts=None, ute=None,
-            scale=None, heads=None) -> Tuple[np.ndarray, np.ndarray]:
+            scale=None, heads=None, sink=None) -> Tuple[np.ndarray, np.ndarray]:
     """O [B,H,Nq,dv] and logsumexp [B,H,Nq] (natural log, scale included).
 
-    q [B,H,Nq,d], k [B,H,Nk,d], v [B,H,Nk,dv], vectors [B,Hm,Nk].
-    ``heads``: optional list of (b, h) pairs to evaluate; other entries stay 0.
+    q [B,H,Nq,d], k [B,H,Nk,d], v [B,H,Nk,dv], vectors [B,Hm,Nk], sink
+    optional [H] logits. ``heads``: optional list of (b, h) pairs to
+    evaluate; other entries stay 0.
     """
     B, H, Nq, _ = q.shape
     Nk = k.shape[2]
@@ -136,18 +150,22 @@ def forward(q, k, v, causal, lts=None, lte=None, uts=None, ute=None,
         o[b, h], lse[b, h] = forward_rows(
             q[b, h], k[b, h], v[b, h], Nk, causal,
             mask_row(lts, b, h), mask_row(lte, b, h),
-            mask_row(uts, b, h), mask_row(ute, b, h), scale=scale)
+            mask_row(uts, b, h), mask_row(ute, b, h), scale=scale,
+            sink=None if sink is None else float(sink[h]))
     return o, lse
 
 
 def backward(q, k, v, do, causal, lts=None, lte=None, uts=None, ute=None,
-             scale=None, heads=None):
-    """Analytic gradients (dQ, dK, dV) of O = softmax(scale Q K^T + M) V given dO.
+             scale=None, heads=None, sink=None):
+    """Analytic gradients (dQ, dK, dV) of O = softmax(scale Q K^T + M) V given dO,
+    and with ``sink`` ([H] logits) also dsink [H].
 
     With P the masked softmax and dP = dO V^T:
       dV = P^T dO,  dS = P * (dP - rowsum(P * dP)),  dQ = scale dS K,
-      dK = scale dS^T Q.
-    Rows with every key masked have P = 0 and so contribute nothing.
+      dK = scale dS^T Q,  dsink_h = -sum_i P_sink,i * rowsum(P * dP)_i,
+    where P_sink,i = exp(s_h - LSE_i) is the sink's share of row i and
+    rowsum(P * dP) = dO_i . O_i. Rows with every key masked have P = 0 and so
+    contribute nothing.
     """
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
@@ -156,6 +174,7 @@ def backward(q, k, v, do, causal, lts=None, lte=None, uts=None, ute=None,
     dk = np.zeros((B, H, Nk, d))
     dvv = np.zeros((B, H, Nk, dv_))
     sc = _scale(d, scale)
+    dsink = np.zeros(H)
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:
         Q = np.asarray(q[b, h], np.float64)
@@ -164,7 +183,8 @@ def backward(q, k, v, do, causal, lts=None, lte=None, uts=None, ute=None,
         dO = np.asarray(do[b, h], np.float64)
         msk = dense_mask(Nk, causal, mask_row(lts, b, h), mask_row(lte, b, h),
                          mask_row(uts, b, h), mask_row(ute, b, h), n_rows=Nq)
-        P, _ = softmax_probs(Q, K, msk, sc)
+        s_h = None if sink is None else float(sink[h])
+        P, lse = softmax_probs(Q, K, msk, sc, s_h)
         del msk
         dvv[b, h] = P.T @ dO
         dP = dO @ V.T
@@ -173,4 +193,8 @@ def backward(q, k, v, do, causal, lts=None, lte=None, uts=None, ute=None,
         del dP, P
         dq[b, h] = sc * (dS @ K)
         dk[b, h] = sc * (dS.T @ Q)
+        if s_h is not None:
+            dsink[h] -= float((np.exp(s_h - lse) * D).sum())
+    if sink is not None:
+        return dq, dk, dvv, dsink
     return dq, dk, dvv
