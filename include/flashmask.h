@@ -155,8 +155,8 @@ fm_status_t flashmask_bwd(const void* q, const void* k, const void* v,
 
 /*
  * Nq query rows against Nk keys (one context-parallel rank's share of the
- * rows: FlashMask-3 abstract). Same contracts as the entry points above with
- * N split in two: Q, O, dO, dQ are [B,H,Nq,*], logsumexp [B,H,Nq]; K, V, dK,
+ * rows: FlashMask-3 abstract), and an optional sink bias. Same contracts as
+ * the entry points above with N split in two: Q, O, dO, dQ are [B,H,Nq,*], logsumexp [B,H,Nq]; K, V, dK,
  * dV are [B,H,Nk,*]; the mask vectors are [B,hm,Nk] and hold bounds on the Nq
  * rows (a missing lte means LTE = Nq; the causal test is j > i). The table is
  * [B,hm,ceil(Nk/block_k),8] and the class map [B,hm,ceil(Nq/block_q),
@@ -173,12 +173,25 @@ fm_status_t flashmask_tile_classify_qk(const int32_t* lts, const int32_t* lte,
                                        int32_t* kblock_minmax, int8_t* tile_class,
                                        void* stream);
 
+/*
+ * sink (nullable, float32 [H], device): sink bias (README "News" names it;
+ * the reading taken here): per head h a logit s_h, in the units of the
+ * scaled scores, joins every row's softmax as one more always-open entry
+ * whose value vector is zero:
+ *     LSE_i = log(exp(s_h) + sum_{open j} exp(scale q_i . k_j)),
+ *     O_i = sum_{open j} exp(scale q_i . k_j - LSE_i) v_j.
+ * A row with nothing open gets O = 0 and LSE = s_h. The backward must get
+ * the same sink (the saved LSE includes it); dsink (nullable, float32 [H],
+ * device, written only when sink is given) receives
+ *     d loss / d s_h = -sum_{b, i} exp(s_h - LSE_i) (dO_i . O_i),
+ * reduced in a fixed order (deterministic).
+ */
 fm_status_t flashmask_fwd_qk(const void* q, const void* k, const void* v,
                              const int32_t* lts, const int32_t* lte,
                              const int32_t* uts, const int32_t* ute, int hm,
                              const int32_t* kblock_minmax,
                              int B, int H, int Nq, int Nk, int d, int dv, fm_dtype_t dtype,
-                             int causal, float softmax_scale,
+                             int causal, float softmax_scale, const float* sink,
                              void* o, float* lse, int64_t* tile_counts,
                              void* workspace, size_t workspace_bytes, void* stream);
 
@@ -188,8 +201,9 @@ fm_status_t flashmask_bwd_qk(const void* q, const void* k, const void* v,
                              const int32_t* uts, const int32_t* ute, int hm,
                              const int32_t* kblock_minmax,
                              int B, int H, int Nq, int Nk, int d, int dv, fm_dtype_t dtype,
-                             int causal, float softmax_scale,
-                             void* dq, void* dk, void* dv_out, int64_t* tile_counts,
+                             int causal, float softmax_scale, const float* sink,
+                             void* dq, void* dk, void* dv_out, float* dsink,
+                             int64_t* tile_counts,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Largest nchunks flashmask_localize accepts. */

@@ -44,11 +44,11 @@ _SIGNATURES = {
     "flashmask_workspace_size_qk": (_c_size_t, [_c_int] * 8 + [_c_int]),
     "flashmask_tile_classify_qk": (_c_int, [_c_void_p] * 4 + [_c_int] * 7 + [_c_void_p, _c_void_p, _c_void_p]),
     "flashmask_fwd_qk": (_c_int, [_c_void_p] * 3 + [_c_void_p] * 4 + [_c_int, _c_void_p]
-                         + [_c_int] * 6 + [_c_int, _c_int, _c_float]
+                         + [_c_int] * 6 + [_c_int, _c_int, _c_float, _c_void_p]
                          + [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "flashmask_bwd_qk": (_c_int, [_c_void_p] * 6 + [_c_void_p] * 4 + [_c_int, _c_void_p]
-                         + [_c_int] * 6 + [_c_int, _c_int, _c_float]
-                         + [_c_void_p] * 4 + [_c_void_p, _c_size_t, _c_void_p]),
+                         + [_c_int] * 6 + [_c_int, _c_int, _c_float, _c_void_p]
+                         + [_c_void_p] * 5 + [_c_void_p, _c_size_t, _c_void_p]),
     "flashmask_max_chunks": (_c_int, []),
     "flashmask_localize": (_c_int, [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p, _c_int]
                            + [_c_void_p] * 4 + [_c_void_p]),
@@ -148,6 +148,14 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _sink(sink: Optional[torch.Tensor], H: int) -> Optional[torch.Tensor]:
+    if sink is None:
+        return None
+    if sink.dtype != torch.float32 or sink.numel() != H:
+        raise ValueError("sink must be float32 with one logit per head")
+    return sink.contiguous()
+
+
 def _check(fn: str, st: int):
     if st != 0:
         raise FlashMaskError(fn, st)
@@ -184,11 +192,12 @@ def tile_classify(mask: Mask, B: int, N: int, block_q: int, block_k: int, classe
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask, scale: Optional[float] = None,
         table: Optional[torch.Tensor] = None, tile_counts: Optional[torch.Tensor] = None,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-        workspace: Optional[torch.Tensor] = None):
+        workspace: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None):
     """O [B,H,Nq,dv] (q's dtype) and logsumexp [B,H,Nq] float32.
 
     q [B,H,Nq,d], k [B,H,Nk,d], v [B,H,Nk,dv]; the mask vectors have Nk
-    entries (Nq == Nk is the plain case)."""
+    entries (Nq == Nk is the plain case). sink: optional float32 [H] sink
+    logits."""
     B, H, N, d = q.shape
     Nk = k.shape[2]
     dv = v.shape[-1]
@@ -203,7 +212,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask, scale: Op
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     st = lib().flashmask_fwd_qk(_ptr(q), _ptr(k), _ptr(v), *_mask_ptrs(mask), mask.hm, _ptr(table),
                                 B, H, N, Nk, d, dv, _dtype_code(q.dtype), int(mask.causal),
-                                0.0 if scale is None else float(scale),
+                                0.0 if scale is None else float(scale), _ptr(_sink(sink, H)),
                                 _ptr(o), _ptr(l), _ptr(tile_counts), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(q.device))
     _check("flashmask_fwd_qk", st)
@@ -212,8 +221,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask, scale: Op
 
 def bwd(q, k, v, o, lse, dout, mask: Mask, scale: Optional[float] = None,
         table: Optional[torch.Tensor] = None, tile_counts: Optional[torch.Tensor] = None,
-        workspace: Optional[torch.Tensor] = None, grads=None):
-    """(dQ, dK, dV) in q's dtype (shapes as in fwd)."""
+        workspace: Optional[torch.Tensor] = None, grads=None, sink: Optional[torch.Tensor] = None):
+    """(dQ, dK, dV) in q's dtype (shapes as in fwd); with a sink also
+    d loss / d sink (float32 [H]) as a fourth result."""
     B, H, N, d = q.shape
     Nk = k.shape[2]
     dv = v.shape[-1]
@@ -223,16 +233,17 @@ def bwd(q, k, v, o, lse, dout, mask: Mask, scale: Optional[float] = None,
         dvv = torch.empty_like(v)
     else:
         dq, dk, dvv = grads
+    dsink = None if sink is None else torch.empty(H, dtype=torch.float32, device=q.device)
     ws_bytes = workspace_size(True, B, H, N, d, dv, mask.hm, q.dtype, Nk=Nk)
     ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     st = lib().flashmask_bwd_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                                 *_mask_ptrs(mask), mask.hm, _ptr(table),
                                 B, H, N, Nk, d, dv, _dtype_code(q.dtype), int(mask.causal),
-                                0.0 if scale is None else float(scale),
-                                _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(tile_counts), _ptr(ws), ws.numel(),
-                                _stream(q.device))
+                                0.0 if scale is None else float(scale), _ptr(_sink(sink, H)),
+                                _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(dsink), _ptr(tile_counts), _ptr(ws),
+                                ws.numel(), _stream(q.device))
     _check("flashmask_bwd_qk", st)
-    return dq, dk, dvv
+    return (dq, dk, dvv) if sink is None else (dq, dk, dvv, dsink)
 
 
 def localize(mask: Mask, B: int, Nk: int, n_rows: int, chunks) -> Mask:

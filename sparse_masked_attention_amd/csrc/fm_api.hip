@@ -145,9 +145,9 @@ fm_status_t flashmask_tile_classify(const int32_t* lts, const int32_t* lte, cons
 fm_status_t flashmask_fwd_qk(const void* q, const void* k, const void* v, const int32_t* lts,
                              const int32_t* lte, const int32_t* uts, const int32_t* ute, int hm,
                              const int32_t* kblock_minmax, int B, int H, int Nq, int Nk, int d,
-                             int dv, fm_dtype_t dtype, int causal, float softmax_scale, void* o,
-                             float* lse, int64_t* tile_counts, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             int dv, fm_dtype_t dtype, int causal, float softmax_scale,
+                             const float* sink, void* o, float* lse, int64_t* tile_counts,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   fm_status_t st = check_common(B, H, Nq, Nk, d, dv, dtype, hm, uts, ute, causal);
   if (st != FM_SUCCESS) return st;
   if ((long long)B * H * Nq == 0) return FM_SUCCESS;
@@ -184,6 +184,7 @@ fm_status_t flashmask_fwd_qk(const void* q, const void* k, const void* v, const 
   a.scale = resolve_scale(softmax_scale, d);
   a.out = o;
   a.lse_out = lse;
+  a.sink = sink;
   a.tile_counts = reinterpret_cast<unsigned long long*>(tile_counts);
   if (fm::launch_fwd(a, s) != hipSuccess) return FM_ERROR_HIP;
   return FM_SUCCESS;
@@ -196,21 +197,28 @@ fm_status_t flashmask_fwd(const void* q, const void* k, const void* v, const int
                           int64_t* tile_counts, void* workspace, size_t workspace_bytes,
                           void* stream) {
   return flashmask_fwd_qk(q, k, v, lts, lte, uts, ute, hm, kblock_minmax, B, H, N, N, d, dv, dtype,
-                          causal, softmax_scale, o, lse, tile_counts, workspace, workspace_bytes,
-                          stream);
+                          causal, softmax_scale, nullptr, o, lse, tile_counts, workspace,
+                          workspace_bytes, stream);
 }
 
 fm_status_t flashmask_bwd_qk(const void* q, const void* k, const void* v, const void* o,
                              const float* lse, const void* dout, const int32_t* lts,
                              const int32_t* lte, const int32_t* uts, const int32_t* ute, int hm,
                              const int32_t* kblock_minmax, int B, int H, int Nq, int Nk, int d,
-                             int dv, fm_dtype_t dtype, int causal, float softmax_scale, void* dq,
-                             void* dk, void* dv_out, int64_t* tile_counts, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             int dv, fm_dtype_t dtype, int causal, float softmax_scale,
+                             const float* sink, void* dq, void* dk, void* dv_out, float* dsink,
+                             int64_t* tile_counts, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   fm_status_t st = check_common(B, H, Nq, Nk, d, dv, dtype, hm, uts, ute, causal);
   if (st != FM_SUCCESS) return st;
   if (!bwd_supported(d, dv, dtype)) return FM_ERROR_NOT_SUPPORTED;
-  if ((long long)B * H * (Nq > Nk ? Nq : Nk) == 0) return FM_SUCCESS;
+  if ((long long)B * H * (Nq > Nk ? Nq : Nk) == 0) {
+    // no row: the sink's gradient is an empty sum
+    if (sink != nullptr && dsink != nullptr && H > 0 &&
+        fm::launch_sink_zero(sink, dsink, H, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+      return FM_ERROR_HIP;
+    return FM_SUCCESS;
+  }
   // the query side (Q, O, LSE, dO, dQ) may be empty, or the key side (K, V, dK, dV)
   if (Nq > 0 && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr))
     return FM_ERROR_INVALID_VALUE;
@@ -258,6 +266,8 @@ fm_status_t flashmask_bwd_qk(const void* q, const void* k, const void* v, const 
   a.dq = dq;
   a.dk = dk;
   a.dv_out = dv_out;
+  a.sink = sink;
+  a.dsink = dsink;
   a.tile_counts = reinterpret_cast<unsigned long long*>(tile_counts);
   if (fm::launch_bwd(a, s) != hipSuccess) return FM_ERROR_HIP;
   return FM_SUCCESS;
@@ -271,8 +281,8 @@ fm_status_t flashmask_bwd(const void* q, const void* k, const void* v, const voi
                           void* dv_out, int64_t* tile_counts, void* workspace,
                           size_t workspace_bytes, void* stream) {
   return flashmask_bwd_qk(q, k, v, o, lse, dout, lts, lte, uts, ute, hm, kblock_minmax, B, H, N, N,
-                          d, dv, dtype, causal, softmax_scale, dq, dk, dv_out, tile_counts,
-                          workspace, workspace_bytes, stream);
+                          d, dv, dtype, causal, softmax_scale, nullptr, dq, dk, dv_out, nullptr,
+                          tile_counts, workspace, workspace_bytes, stream);
 }
 
 int flashmask_max_chunks(void) { return fm::kMaxChunks; }

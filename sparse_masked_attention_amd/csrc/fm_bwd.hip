@@ -689,6 +689,51 @@ static hipError_t launch_bwd_f32(BwdParams p, hipStream_t stream) {
   return launch_convert<float>(p, D, stream);
 }
 
+// ---------------------------------------------------------------- sink gradient
+// d loss / d s_h = -sum over the head's rows of exp(s_h - LSE_i) * delta_i:
+// the sink is one more softmax entry with a zero value vector, so its share
+// of row i is exp(s_h - LSE_i) and d O_i / d s_h = -that share * O_i. One
+// workgroup per head, a fixed summation order (per-thread strides, then
+// wave shuffles, then the 4 waves in order): deterministic. `have_rows` is
+// false when no row saw a key (then every O_i, and so every term, is 0).
+__global__ __launch_bounds__(256) void sink_grad_kernel(const float* __restrict__ lse2,
+                                                        const float* __restrict__ delta,
+                                                        const float* __restrict__ sink,
+                                                        float* __restrict__ dsink, int B, int H,
+                                                        int Nq, int have_rows) {
+  const int h = blockIdx.x;
+  const float s2 = sink[h] * kLog2e;
+  float acc = 0.f;
+  if (have_rows) {
+    for (int b = 0; b < B; ++b) {
+      const long long base = ((long long)b * H + h) * Nq;
+      for (int i = threadIdx.x; i < Nq; i += 256) acc += exp2f(s2 - lse2[base + i]) * delta[base + i];
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) dsink[h] = -(((part[0] + part[1]) + part[2]) + part[3]);
+}
+
+static hipError_t launch_sink_grad(const AttnArgs& a, bool have_rows, hipStream_t stream) {
+  if (a.sink == nullptr || a.dsink == nullptr || a.H == 0) return hipSuccess;
+  hipLaunchKernelGGL(sink_grad_kernel, dim3((unsigned)a.H), dim3(256), 0, stream, a.lse2, a.delta,
+                     a.sink, a.dsink, a.B, a.H, a.Nq, have_rows ? 1 : 0);
+  return hipGetLastError();
+}
+
+// dsink = 0 for a problem with no query row or no batch element
+hipError_t launch_sink_zero(const float* sink, float* dsink, int H, hipStream_t stream) {
+  AttnArgs a{};
+  a.sink = sink;
+  a.dsink = dsink;
+  a.H = H;
+  return launch_sink_grad(a, false, stream);
+}
+
 // ---------------------------------------------------------------- zero fill
 // Gradients of a side with no partner (no keys, or no query rows) are zero.
 __global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ p, long long n16) {
@@ -707,14 +752,29 @@ static hipError_t launch_zero(void* p, long long bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
+static hipError_t launch_bwd_main(const AttnArgs& a, hipStream_t stream);
+
 hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream) {
   const long long elt = a.is_bf16 ? 2 : 4;
-  if (a.Nk == 0) return launch_zero(a.dq, (long long)a.B * a.H * a.Nq * a.d * elt, stream);
-  if (a.Nq == 0) {
-    const hipError_t e = launch_zero(a.dk, (long long)a.B * a.H * a.Nk * a.d * elt, stream);
+  if (a.Nk == 0) {
+    const hipError_t e = launch_zero(a.dq, (long long)a.B * a.H * a.Nq * a.d * elt, stream);
     if (e != hipSuccess) return e;
-    return launch_zero(a.dv_out, (long long)a.B * a.H * a.Nk * a.dv * elt, stream);
+    return launch_sink_grad(a, false, stream);
   }
+  if (a.Nq == 0) {
+    hipError_t e = launch_zero(a.dk, (long long)a.B * a.H * a.Nk * a.d * elt, stream);
+    if (e != hipSuccess) return e;
+    e = launch_zero(a.dv_out, (long long)a.B * a.H * a.Nk * a.dv * elt, stream);
+    if (e != hipSuccess) return e;
+    return launch_sink_grad(a, false, stream);
+  }
+  const hipError_t e = launch_bwd_main(a, stream);
+  if (e != hipSuccess) return e;
+  // delta and the base-2 LSE are in the workspace now (dQ pass or preprocess)
+  return launch_sink_grad(a, true, stream);
+}
+
+static hipError_t launch_bwd_main(const AttnArgs& a, hipStream_t stream) {
   BwdParams p{};
   p.q = a.q;
   p.k = a.k;

@@ -39,6 +39,7 @@ struct FwdParams {
   const int32_t* table;  // [B, hm, nkb, 8] at 64-column blocks
   void* o;
   float* lse;
+  const float* sink;     // forward: per-head sink logits [H], or nullptr
   unsigned long long* counts;
   // dQ mode (backward): dO and the forward's O and natural-log LSE in; dQ
   // out, and per row the base-2 LSE and delta = rowsum(dO * O) out for the
@@ -80,6 +81,32 @@ __device__ inline void mask_block(f32x16& s, const FM_LDS int* vl, int kl0, int 
       if (m) s[4 * g + e] = kNegInf;
     }
   }
+}
+
+// ---------------------------------------------------------------- row epilogue
+// From a row's sum lt of exp(S - m) over its open keys (m the running
+// offset, in raw score units before `scale`): the factor that turns the
+// accumulated sum of P V into O, and the natural-log LSE. With a sink logit
+// s (one more always-open entry with a zero value vector) the normaliser
+// becomes exp(lse0) + exp(s): LSE = logaddexp(lse0, s), computed in the log
+// domain so a large s cannot overflow, and O shrinks by exp(lse0 - LSE). A
+// row with nothing open has O = 0 and LSE = -inf (s with a sink).
+__device__ inline void finish_row(float lt, float m, float scale, float s, bool has_sink,
+                                  float& inv, float& lse) {
+  if (!(lt > 0.f)) {
+    inv = 0.f;
+    lse = has_sink ? s : kNegInf;
+    return;
+  }
+  const float lse0 = m * scale + __logf(lt);
+  if (!has_sink) {
+    inv = 1.f / lt;
+    lse = lse0;
+    return;
+  }
+  const float hi = fmaxf(lse0, s);
+  lse = hi + log1pf(__expf(-fabsf(lse0 - s)));
+  inv = __expf(lse0 - lse) / lt;
 }
 
 // ---------------------------------------------------------------- bf16 kernel
@@ -460,7 +487,8 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
   if constexpr (!DQ) {
     // normalise, store O (bf16) and the natural-log LSE
     const float lt = sum_x32(l_run);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float inv, row_lse;
+    finish_row(lt, m_run, p.scale, p.sink != nullptr ? p.sink[h] : kNegInf, p.sink != nullptr, inv, row_lse);
     if (i < Nq) {
       bf16* og = reinterpret_cast<bf16*>(p.o) + (qslice + i) * DV;
 #pragma unroll
@@ -472,7 +500,7 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
           for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[mb][4 * g + e] * inv);
           *reinterpret_cast<bf16x4*>(og + 32 * mb + 8 * g + 4 * hh) = v4;
         }
-      if (hh == 0) p.lse[qslice + i] = lt > 0.f ? m_run * p.scale + __logf(lt) : kNegInf;
+      if (hh == 0) p.lse[qslice + i] = row_lse;
     }
   } else {
     // dQ = scale * dS K
@@ -607,7 +635,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
   }
 
   const float lt = sum_x32(l_run);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  float inv, row_lse;
+  finish_row(lt, m_run, p.scale, p.sink != nullptr ? p.sink[h] : kNegInf, p.sink != nullptr, inv, row_lse);
   if (i < Nq) {
     float* og = reinterpret_cast<float*>(p.o) + (qslice + i) * D;
 #pragma unroll
@@ -619,7 +648,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
         for (int e = 0; e < 4; ++e) v4[e] = oacc[mb][4 * g + e] * inv;
         *reinterpret_cast<f32x4*>(og + 32 * mb + 8 * g + 4 * hh) = v4;
       }
-    if (hh == 0) p.lse[qslice + i] = lt > 0.f ? m_run * p.scale + logf(lt) : kNegInf;
+    if (hh == 0) p.lse[qslice + i] = row_lse;
   }
   if (p.counts != nullptr && tid == 0) {
     atomicAdd(p.counts + 0, (unsigned long long)cnt0);
@@ -668,6 +697,7 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
   p.table = a.table;
   p.o = a.out;
   p.lse = a.lse_out;
+  p.sink = a.sink;
   p.counts = a.tile_counts;
   p.B = a.B;
   p.H = a.H;

@@ -53,6 +53,8 @@ struct AttnArgs {
   float* dq_acc;      // backward workspace (fp32 path): float32 [B, H, N, d]
   float* delta;       // backward workspace: float32 [B, H, N]
   float* lse2;        // backward workspace: float32 [B, H, N], base-2 logsumexp
+  const float* sink;  // per-head sink logits [H] or nullptr
+  float* dsink;       // backward: d loss / d sink [H] or nullptr
   unsigned long long* tile_counts;
 };
 
@@ -68,6 +70,7 @@ hipError_t launch_localize(const MaskArgs& m, int B, int Nk, int n_rows, const i
                            int32_t* ute_o, hipStream_t stream);
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_sink_zero(const float* sink, float* dsink, int H, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace fm

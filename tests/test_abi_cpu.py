@@ -153,14 +153,14 @@ def test_rectangular_workspace_and_empty_sides(lib):
     assert _binding.workspace_size(False, 1, 2, 100, 128, 128, 1, torch.bfloat16, Nk=0) == 0
     p = lambda x: None if x is None else ctypes.c_void_p(x * 256)
     fwd = lambda Nq, Nk, q=1: lib.flashmask_fwd_qk(p(q), p(1), p(1), p(1), None, None, None, 1, None,
-                                                   1, 2, Nq, Nk, 128, 128, 1, 1, 0.0, p(1), p(1),
+                                                   1, 2, Nq, Nk, 128, 128, 1, 1, 0.0, None, p(1), p(1),
                                                    None, p(1), 1 << 30, None)
     assert fwd(0, 64, q=None) == FM_SUCCESS       # no query row: nothing to do
     assert fwd(16, -1) == FM_INVALID
     assert fwd(-1, 16) == FM_INVALID
     bwd = lambda Nq, Nk: lib.flashmask_bwd_qk(p(1), p(1), p(1), p(1), p(1), p(1), p(1), None, None,
-                                              None, 1, None, 1, 2, Nq, Nk, 128, 128, 1, 1, 0.0,
-                                              p(1), p(1), p(1), None, p(1), 1 << 30, None)
+                                              None, 1, None, 1, 2, Nq, Nk, 128, 128, 1, 1, 0.0, None,
+                                              p(1), p(1), p(1), None, None, p(1), 1 << 30, None)
     assert bwd(0, 0) == FM_SUCCESS
     assert bwd(-3, 5) == FM_INVALID
 
