@@ -291,74 +291,121 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib) sacc[ib] = f32x16{};
     }
-    // S = Q K^T + bias and dP = dO V^T for rows 32 ib .. 32 ib + 31
-    auto sdp = [&](int ib) {
+    // Every MFMA below takes one operand from LDS. Those operands are read
+    // PF MFMAs ahead through a ring of registers, in source order: with
+    // registers this short the compiler keeps the written order, so the
+    // order written here is the one that runs. extra(t) is VALU work for
+    // the other row half, placed after MFMA t.
+    constexpr int PF = 4;
+    // Left alone, the scheduler sinks each read to just before its MFMA to
+    // save registers, and every MFMA then waits out a full LDS latency. A
+    // fence per step keeps reads and MFMAs where they are written; VALU,
+    // SALU and transcendental work may still cross (mask 0x406).
+    auto step_fence = [] { __builtin_amdgcn_sched_barrier(0x406); };
+    // S = Q K^T + bias and dP = dO V^T for rows 32 ib .. 32 ib + 31; the two
+    // accumulation chains alternate while both have steps left
+    constexpr int NS = D / 16, NP = DV / 16, NSP = NS + NP, NSPMIN = NS < NP ? NS : NP;
+    static_assert(NSP >= PF, "prefetch ring deeper than the S / dP steps");
+    auto sdp = [&](int ib, auto extra) {
       dpacc[ib] = f32x16{};
       const int row = 32 * ib + l32;
+      auto is_s = [](int t) { return t < 2 * NSPMIN ? (t & 1) == 0 : NS > NP; };
+      auto chunk = [](int t) { return t < 2 * NSPMIN ? t >> 1 : t - NSPMIN; };
+      auto rd = [&](int t) {
+        return is_s(t) ? lds_read_b128(tile_addr<D>(qst, row, 16 * chunk(t) + 8 * hh))
+                       : lds_read_b128(tile_addr<DV>(dost, row, 16 * chunk(t) + 8 * hh));
+      };
+      bf16x8 ring[PF];
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-        sacc[ib] = mfma32(lds_read_b128(tile_addr<D>(qst, row, 16 * c + 8 * hh)), kB[c], sacc[ib]);
+      for (int t = 0; t < PF; ++t) ring[t] = rd(t);
 #pragma unroll
-      for (int c = 0; c < DV / 16; ++c)
-        dpacc[ib] = mfma32(lds_read_b128(tile_addr<DV>(dost, row, 16 * c + 8 * hh)), vB[c], dpacc[ib]);
+      for (int t = 0; t < NSP; ++t) {
+        const bf16x8 a = ring[t % PF];
+        if (t + PF < NSP) ring[t % PF] = rd(t + PF);
+        if (is_s(t)) sacc[ib] = mfma32(a, kB[chunk(t)], sacc[ib]);
+        else dpacc[ib] = mfma32(a, vB[chunk(t)], dpacc[ib]);
+        extra(t);
+        step_fence();
+      }
     };
     // P = exp2(S * scale * log2e - LSE2) and dS = P (dP - delta), as bf16
-    // B operands; fully masked rows have LSE2 = +inf
-    auto probs = [&](int ib) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rl = 32 * ib + 8 * g + 4 * hh;   // first of 4 rows held
-        const f32x4 lse4 = *reinterpret_cast<const FM_LDS f32x4*>(lse_l + rl);
-        const f32x4 del4 = *reinterpret_cast<const FM_LDS f32x4*>(del_l + rl);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          const float pv = fast_exp2(__builtin_fmaf(sacc[ib][r], p.sl2, -lse4[e]));
-          pB[2 * ib + r / 8][r % 8] = (bf16)pv;
-          dsB[2 * ib + r / 8][r % 8] = (bf16)(pv * (dpacc[ib][r] - del4[e]));
-        }
-      }
+    // B operands, one accumulator register r of half ib at a time; fully
+    // masked rows have LSE2 = +inf. Registers 4 g .. 4 g + 3 hold 4
+    // consecutive rows whose LSE2 and delta come as one 16-byte read each,
+    // issued one group ahead.
+    f32x4 lsev[4], delv[4];
+    auto probs_read = [&](int ib, int g) {
+      const int rl = 32 * ib + 8 * g + 4 * hh;   // first of the 4 rows
+      lsev[g] = *reinterpret_cast<const FM_LDS f32x4*>(lse_l + rl);
+      delv[g] = *reinterpret_cast<const FM_LDS f32x4*>(del_l + rl);
     };
-    // dV += P^T dO and dK += dS^T Q over the 16 rows of chunk c; dO / Q
-    // operands by transposed reads
+    auto probs_row = [&](int ib, int r) {
+      const int g = r / 4, e = r % 4;
+      if (e == 0 && g + 1 < 4) probs_read(ib, g + 1);
+      const float pv = fast_exp2(__builtin_fmaf(sacc[ib][r], p.sl2, -lsev[g][e]));
+      pB[2 * ib + r / 8][r % 8] = (bf16)pv;
+      dsB[2 * ib + r / 8][r % 8] = (bf16)(pv * (dpacc[ib][r] - delv[g][e]));
+    };
+    // the 16 rows of half ib spread evenly over NT MFMA steps
+    auto probs_spread = [&](int ib, int t, int NT) {
+#pragma unroll
+      for (int r = (16 * t + NT - 1) / NT; r < (16 * (t + 1) + NT - 1) / NT; ++r) probs_row(ib, r);
+    };
+    // dV += P^T dO and dK += dS^T Q over the 16-row chunks cc and cc + 1; the
+    // dO / Q operands come by transposed reads, and dV and dK steps alternate
+    // while both have steps left
+    constexpr int NV2 = C::DVO / 32, NK2 = C::DO / 32, NC = NV2 + NK2;
+    constexpr int NCMIN = NV2 < NK2 ? NV2 : NK2;
+    static_assert(2 * NC >= PF, "prefetch ring deeper than the dV / dK steps");
     const int sl = lane & 15;
-    auto dvdk = [&](int c) {
-      const int ra = 16 * c + 4 * hh + (sl >> 2);
-      const int rb = ra + 8;
-      const int cl = 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+    const int cl = 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+    auto dvdk = [&](int cc, auto extra) {
+      auto is_v = [](int u) { return u < 2 * NCMIN ? (u & 1) == 0 : NV2 > NK2; };
+      auto mblk = [](int u) { return u < 2 * NCMIN ? u >> 1 : u - NCMIN; };
+      auto rd = [&](int t) {
+        const int c = cc + t / NC, u = t % NC;
+        const int ra = 16 * c + 4 * hh + (sl >> 2);
+        const int rb = ra + 8;
+        if (is_v(u)) {
+          const int col = col0v + 32 * mblk(u) + cl;
+          return cat(lds_read_tr(tile_addr<DV>(dost, ra, col)), lds_read_tr(tile_addr<DV>(dost, rb, col)));
+        }
+        const int col = col0 + 32 * mblk(u) + cl;
+        return cat(lds_read_tr(tile_addr<D>(qst, ra, col)), lds_read_tr(tile_addr<D>(qst, rb, col)));
+      };
+      bf16x8 ring[PF];
 #pragma unroll
-      for (int mb = 0; mb < C::DVO / 32; ++mb) {
-        const int col = col0v + 32 * mb + cl;
-        const bf16x8 bo = cat(lds_read_tr(tile_addr<DV>(dost, ra, col)), lds_read_tr(tile_addr<DV>(dost, rb, col)));
-        dvacc[mb] = mfma32(pB[c], bo, dvacc[mb]);
-      }
+      for (int t = 0; t < PF; ++t) ring[t] = rd(t);
 #pragma unroll
-      for (int mb = 0; mb < C::DO / 32; ++mb) {
-        const int col = col0 + 32 * mb + cl;
-        const bf16x8 bq = cat(lds_read_tr(tile_addr<D>(qst, ra, col)), lds_read_tr(tile_addr<D>(qst, rb, col)));
-        dkacc[mb] = mfma32(dsB[c], bq, dkacc[mb]);
+      for (int t = 0; t < 2 * NC; ++t) {
+        const bf16x8 a = ring[t % PF];
+        if (t + PF < 2 * NC) ring[t % PF] = rd(t + PF);
+        const int c = cc + t / NC, u = t % NC;
+        if (is_v(u)) dvacc[mblk(u)] = mfma32(pB[c], a, dvacc[mblk(u)]);
+        else dkacc[mblk(u)] = mfma32(dsB[c], a, dkacc[mblk(u)]);
+        extra(t);
+        step_fence();
       }
     };
-    // Software-pipelined over the two row halves, so the exponentials of
-    // one half run on the VALU while the MFMAs of the other run; the
-    // scheduling fences keep the compiler from regrouping the phases.
-    sdp(0);
+    // Pipelined over the two row halves: the exponentials of one half run on
+    // the VALU between the MFMAs of the other; the scheduling fences keep
+    // the compiler from regrouping the phases.
+    auto none = [](int) {};
+    sdp(0, none);
     __builtin_amdgcn_sched_barrier(0);
+    probs_read(0, 0);
     if constexpr (NIB == 2) {
-      sdp(1);
-      probs(0);
+      sdp(1, [&](int t) { probs_spread(0, t, NSP); });
       __builtin_amdgcn_sched_barrier(0);
-      dvdk(0);
-      dvdk(1);
-      probs(1);
+      probs_read(1, 0);
+      dvdk(0, [&](int t) { probs_spread(1, t, 2 * NC); });
       __builtin_amdgcn_sched_barrier(0);
-      dvdk(2);
-      dvdk(3);
+      dvdk(2, none);
     } else {
-      probs(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) probs_row(0, r);
       __builtin_amdgcn_sched_barrier(0);
-      dvdk(0);
-      dvdk(1);
+      dvdk(0, none);
     }
   };
 

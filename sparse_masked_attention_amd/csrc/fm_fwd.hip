@@ -342,11 +342,27 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
         f32x16 s, dp = f32x16{};
         bias(s, jb);
         const int row = jb * 32 + l32;
-        // S^T = K Q^T + bias, dP^T = V dO^T
+        // S^T = K Q^T + bias, dP^T = V dO^T. The two chains alternate while
+        // both have steps left, and the K / V operands are read PF MFMAs
+        // ahead through a ring of registers (at two waves per SIMD a deeper
+        // ring, or fencing the order, spills registers).
+        constexpr int PF = 2;
+        constexpr int NS = D / 16, NP = DV / 16, NSP = NS + NP, NMIN = NS < NP ? NS : NP;
+        auto is_s = [](int t) { return t < 2 * NMIN ? (t & 1) == 0 : NS > NP; };
+        auto chunk = [](int t) { return t < 2 * NMIN ? t >> 1 : t - NMIN; };
+        auto rd = [&](int t) {
+          return is_s(t) ? row_read(KW{}, kst, row, 2 * chunk(t) + hh) : row_read(VW{}, vst, row, 2 * chunk(t) + hh);
+        };
+        bf16x8 ring[PF];
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) s = mfma32(row_read(KW{}, kst, row, 2 * c + hh), qf[c], s);
+        for (int t = 0; t < PF; ++t) ring[t] = rd(t);
 #pragma unroll
-        for (int c = 0; c < DV / 16; ++c) dp = mfma32(row_read(VW{}, vst, row, 2 * c + hh), dof[c], dp);
+        for (int t = 0; t < NSP; ++t) {
+          const bf16x8 a = ring[t % PF];
+          if (t + PF < NSP) ring[t % PF] = rd(t + PF);
+          if (is_s(t)) s = mfma32(a, qf[chunk(t)], s);
+          else dp = mfma32(a, dof[chunk(t)], dp);
+        }
         // dS = P (dP - delta) with P = exp2(S * scale * log2e - LSE2)
         bf16x8 pf[2];
 #pragma unroll
