@@ -499,8 +499,47 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   }
 
   wait_vmcnt<0>();  // no load into LDS may still be in flight when the wave ends
-  // --- write dK = scale * dS^T Q and dV for this wave's keys
-  if (wc0 < Nk) {
+  // --- write dK = scale * dS^T Q and dV for this wave's keys. A lane holds
+  // one column of 16 keys, so stores straight from registers write 2 bytes
+  // per lane. Where they fit, the rows go through LDS instead (the stage
+  // buffers are free: every wave has passed its final barrier and no load
+  // into LDS is in flight) and each store writes whole rows, 16 bytes per
+  // lane: dK of the 4 waves in stage 0, dV in stage 1.
+  constexpr bool kStaged = 4 * 32 * C::DO * 2 <= C::STAGE && 4 * 32 * C::DVO * 2 <= C::STAGE;
+  if constexpr (kStaged) {
+    // key row kr, 16-byte chunk c of a W-wide row at kr * W * 2 + 16 (c ^ (kr & 7))
+    auto stage_rows = [&](FM_LDS char* base, const f32x16* acc, float mul, auto w_c) {
+      constexpr int W = decltype(w_c)::value;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 8 * (r / 4) + 4 * hh + (r % 4);
+#pragma unroll
+        for (int mb = 0; mb < W / 32; ++mb) {
+          const int col = 32 * mb + l32;
+          *reinterpret_cast<FM_LDS bf16*>(base + kr * W * 2 + (((col >> 3) ^ (kr & 7)) << 4) + (col & 7) * 2) =
+              (bf16)(acc[mb][r] * mul);
+        }
+      }
+    };
+    auto store_rows = [&](const FM_LDS char* base, bf16* g, int ld, auto w_c) {
+      constexpr int W = decltype(w_c)::value;
+      constexpr int CH = W / 8;
+#pragma unroll
+      for (int k = 0; k < CH / 2; ++k) {
+        const int f = 64 * k + lane;
+        const int row = f / CH, c = f % CH;
+        const u32x4 val = *reinterpret_cast<const FM_LDS u32x4*>(base + row * W * 2 + ((c ^ (row & 7)) << 4));
+        if (wc0 + row < Nk) *reinterpret_cast<u32x4*>(g + (long long)(wc0 + row) * ld + 8 * c) = val;
+      }
+    };
+    FM_LDS char* kst = (FM_LDS char*)stage0 + w * 32 * C::DO * 2;
+    FM_LDS char* vst = (FM_LDS char*)stage1 + w * 32 * C::DVO * 2;
+    stage_rows(kst, dkacc, p.scale, std::integral_constant<int, C::DO>{});
+    stage_rows(vst, dvacc, 1.f, std::integral_constant<int, C::DVO>{});
+    __builtin_amdgcn_wave_barrier();
+    store_rows(kst, reinterpret_cast<bf16*>(p.dk) + kslice * D + col0, D, std::integral_constant<int, C::DO>{});
+    store_rows(vst, reinterpret_cast<bf16*>(p.dv) + kslice * DV + col0v, DV, std::integral_constant<int, C::DVO>{});
+  } else if (wc0 < Nk) {
     bf16* dkg = reinterpret_cast<bf16*>(p.dk) + kslice * D;
     bf16* dvg = reinterpret_cast<bf16*>(p.dv) + kslice * DV;
 #pragma unroll

@@ -499,39 +499,45 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
     }
   }
 
-  // --- epilogue
+  // --- epilogue: each wave writes its 32 rows of O (or dQ). A lane holds
+  // its own row, 4 consecutive columns per register group, so stores straight
+  // from registers would touch 32 rows per instruction. The rows go through
+  // LDS instead (the stage buffers are free once the last tile is done: every
+  // wave has passed its final barrier and no load into LDS is in flight), and
+  // each store then writes whole rows, 16 bytes per lane.
+  constexpr int W = DQ ? D : DV;   // output row width
+  constexpr int CH = W / 8;        // 16-byte chunks per row
+  static_assert(2 * 32 * W * 2 <= C::STAGE, "two waves' rows fit one stage");
+  float mul;
   if constexpr (!DQ) {
     // normalise, store O (bf16) and the natural-log LSE
     const float lt = sum_x32(l_run);
-    float inv, row_lse;
-    finish_row(lt, m_run, p.scale, p.sink != nullptr ? p.sink[h] : kNegInf, p.sink != nullptr, inv, row_lse);
-    if (i < Nq) {
-      bf16* og = reinterpret_cast<bf16*>(p.o) + (qslice + i) * DV;
-#pragma unroll
-      for (int mb = 0; mb < DV / 32; ++mb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[mb][4 * g + e] * inv);
-          *reinterpret_cast<bf16x4*>(og + 32 * mb + 8 * g + 4 * hh) = v4;
-        }
-      if (hh == 0) p.lse[qslice + i] = row_lse;
-    }
+    float row_lse;
+    finish_row(lt, m_run, p.scale, p.sink != nullptr ? p.sink[h] : kNegInf, p.sink != nullptr, mul, row_lse);
+    if (i < Nq && hh == 0) p.lse[qslice + i] = row_lse;
   } else {
-    // dQ = scale * dS K
-    if (i < Nq) {
-      bf16* dqg = reinterpret_cast<bf16*>(p.dq) + (qslice + i) * D;
+    mul = p.scale;   // dQ = scale * dS K
+  }
+  FM_LDS char* ost = (FM_LDS char*)(w < 2 ? stage0 : stage1) + (w & 1) * 32 * W * 2;
+  // row r, chunk c at r * W * 2 + 16 (c ^ (r & 7)): rows spread over the banks
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
+  for (int mb = 0; mb < W / 32; ++mb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 v4;
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[mb][4 * g + e] * p.scale);
-          *reinterpret_cast<bf16x4*>(dqg + 32 * mb + 8 * g + 4 * hh) = v4;
-        }
+      for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[mb][4 * g + e] * mul);
+      const int col = 32 * mb + 8 * g + 4 * hh;
+      *reinterpret_cast<FM_LDS bf16x4*>(ost + l32 * W * 2 + (((col >> 3) ^ (l32 & 7)) << 4) + (col & 7) * 2) = v4;
     }
+  __builtin_amdgcn_wave_barrier();
+  bf16* outg = reinterpret_cast<bf16*>(DQ ? p.dq : p.o) + (qslice + wr0) * W;
+#pragma unroll
+  for (int k = 0; k < CH / 2; ++k) {
+    const int f = 64 * k + lane;
+    const int row = f / CH, c = f % CH;
+    const u32x4 val = *reinterpret_cast<const FM_LDS u32x4*>(ost + row * W * 2 + ((c ^ (row & 7)) << 4));
+    if (wr0 + row < Nq) *reinterpret_cast<u32x4*>(outg + (long long)row * W + 8 * c) = val;
   }
   if (p.counts != nullptr) {
     atomicAdd(&wcount[0], cnt0);
