@@ -137,11 +137,10 @@ fm_status_t flashmask_fwd(const void* q, const void* k, const void* v,
  * the analytic gradient of O = softmax(scale Q K^T + M) V,
  *   dV = P^T dO, dS = P * (dO V^T - rowsum(dO * O)), dQ = scale dS K,
  *   dK = scale dS^T Q.
- * tile_counts as in the forward, for flashmask_tile_shape(1, ...). For bf16
- * all three gradients are bitwise deterministic (dQ comes from a query-major
- * pass, dK and dV from a key-major pass; no atomics). For fp32, dq is
- * accumulated with float32 atomics, so its bits may vary between runs within
- * rounding; dk and dv_out are deterministic.
+ * tile_counts as in the forward, for flashmask_tile_shape(1, ...). All
+ * three gradients are bitwise deterministic for both dtypes: dQ comes from a
+ * query-major pass and dK, dV from a key-major pass, each summing in a fixed
+ * order in registers (no atomics).
  */
 fm_status_t flashmask_bwd(const void* q, const void* k, const void* v,
                           const void* o, const float* lse, const void* dout,

@@ -104,8 +104,6 @@ size_t flashmask_workspace_size_qk(int is_bwd, int B, int H, int Nq, int Nk, int
   size_t bytes = align_up(table_bytes(B, hm, Nk));
   if (is_bwd) {
     bytes += 2 * align_up((size_t)B * H * Nq * sizeof(float));             // delta, base-2 LSE
-    if (dtype == FM_FP32)
-      bytes += align_up((size_t)B * H * Nq * (size_t)d * sizeof(float));   // dQ accumulator
   }
   return bytes;
 }
@@ -246,8 +244,6 @@ fm_status_t flashmask_bwd_qk(const void* q, const void* k, const void* v, const 
   a.delta = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)B * H * Nq * sizeof(float));
   a.lse2 = reinterpret_cast<float*>(ws);
-  ws += align_up((size_t)B * H * Nq * sizeof(float));
-  a.dq_acc = dtype == FM_FP32 ? reinterpret_cast<float*>(ws) : nullptr;
   a.q = q;
   a.k = k;
   a.v = v;

@@ -43,7 +43,6 @@ struct BwdParams {
   const int32_t* uts;
   const int32_t* ute;
   const int32_t* table;  // [B, hm, ceil(Nk/64), 8]
-  float* dq_acc;     // fp32 path only
   float* delta;
   float* lse2;       // logsumexp in base-2 units; +inf for fully masked rows
   void* dq;
@@ -58,9 +57,9 @@ struct BwdParams {
 
 // ---------------------------------------------------------------- preprocess
 // fp32 path: delta_i = sum_m dO[i][m] * O[i][m] in float32; LSE in base-2
-// units (+inf where the row is fully masked, so exp2(s - LSE2) is 0 there);
-// zero the dQ accumulator rows. 16 threads per row, 16-byte chunks. (The
-// bf16 path computes delta and the base-2 LSE inside its dQ pass.)
+// units (+inf where the row is fully masked, so exp2(s - LSE2) is 0 there).
+// 16 threads per row, 16-byte chunks. (The bf16 path computes delta and the
+// base-2 LSE inside its dQ pass.)
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   const long long rows = (long long)p.B * p.H * p.Nq;
@@ -85,11 +84,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
         for (int e = 0; e < 4; ++e) acc += x[e] * y[e];
       }
     }
-    if constexpr (sizeof(T) == 4) {
-      float* dqa = p.dq_acc + row * D;
-#pragma unroll
-      for (int c = t; c < D / 4; c += 16) *reinterpret_cast<f32x4*>(dqa + 4 * c) = f32x4{};
-    }
   }
 #pragma unroll
   for (int s = 8; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 16);
@@ -97,24 +91,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
     p.delta[row] = acc;
     const float l = p.lse[row];
     p.lse2[row] = l == kNegInf ? __builtin_inff() : l * kLog2e;
-  }
-}
-
-// ---------------------------------------------------------------- dQ convert
-template <typename T>
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ src, T* __restrict__ dst,
-                                                         long long n4) {
-  for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < n4;
-       idx += (long long)gridDim.x * blockDim.x) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(src)[idx];
-    if constexpr (sizeof(T) == 2) {
-      bf16x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
-      reinterpret_cast<bf16x4*>(dst)[idx] = o;
-    } else {
-      reinterpret_cast<f32x4*>(dst)[idx] = v;
-    }
   }
 }
 
@@ -565,16 +541,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- fp32 kernel
-// Same decomposition with v_mfma_f32_32x32x2_f32 and everything staged
-// through LDS with plain loads (no pipelining): 4 waves x 32 keys, query
-// steps of 32 rows. K and V of the lane's key sit in registers as B operands.
+// dK and dV of the fp32 backward (dQ comes from the query-major fp32 dQ
+// pass): the same key-major decomposition with v_mfma_f32_32x32x2_f32 and
+// everything staged through LDS with plain loads (no pipelining): 4 waves x
+// 32 keys, query steps of 32 rows. K and V of the lane's key sit in
+// registers as B operands.
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_f32_kernel(BwdParams p) {
-  constexpr int NW = 4, KW = 32, BKC = 128, BQ = 32, S1 = D + 1, DSS = BKC + 1;
+  constexpr int KW = 32, BKC = 128, BQ = 32, S1 = D + 1;
   __shared__ float qs[BQ * S1];
   __shared__ float dos[BQ * S1];
-  __shared__ float ks[BKC * S1];
-  __shared__ float dss[BQ * DSS];
   __shared__ float lse_s[BQ];
   __shared__ float del_s[BQ];
 
@@ -598,10 +574,6 @@ __global__ __launch_bounds__(256, 1) void bwd_f32_kernel(BwdParams p) {
   const float* vg = reinterpret_cast<const float*>(p.v) + kslice * D;
   const float* dog = reinterpret_cast<const float*>(p.dout) + qslice * D;
 
-  for (int t = tid; t < BKC * D; t += 256) {
-    const int row = t / D, col = t % D;
-    ks[row * S1 + col] = c0 + row < Nk ? kg[(long long)(c0 + row) * D + col] : 0.f;
-  }
   float kr[D / 2], vr[D / 2];
 #pragma unroll
   for (int t = 0; t < D / 2; ++t) {
@@ -695,21 +667,6 @@ __global__ __launch_bounds__(256, 1) void bwd_f32_kernel(BwdParams p) {
           dkacc[mb] = mfma32f(dsr[t], qs[il * S1 + 32 * mb + l32], dkacc[mb]);
         }
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dss[(8 * (r / 4) + 4 * hh + (r % 4)) * DSS + KW * w + l32] = dsr[r];
-    __syncthreads();
-    // dQ over the 128 keys; output blocks of 32 columns spread over the waves
-    for (int mb = w; mb < D / 32; mb += NW) {
-      f32x16 dq = f32x16{};
-#pragma unroll 8
-      for (int t = 0; t < BKC / 2; ++t)
-        dq = mfma32f(dss[l32 * DSS + 2 * t + hh], ks[(2 * t + hh) * S1 + 32 * mb + l32], dq);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = q0 + 8 * (r / 4) + 4 * hh + (r % 4);
-        if (i < Nq) unsafeAtomicAdd(p.dq_acc + (qslice + i) * D + 32 * mb + l32, dq[r]);
-      }
-    }
   }
   if (wc0 < Nk) {
     float* dkg = reinterpret_cast<float*>(p.dk) + kslice * D;
@@ -741,16 +698,6 @@ static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t launch_convert(const BwdParams& p, int d, hipStream_t stream) {
-  const long long n4 = (long long)p.B * p.H * p.Nq * d / 4;
-  long long blocks = (n4 + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL((dq_convert_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, stream, p.dq_acc,
-                     reinterpret_cast<T*>(p.dq), n4);
-  return hipGetLastError();
-}
-
 template <int D, int DV>
 static hipError_t launch_bwd_bf16(BwdParams p, const AttnArgs& a, hipStream_t stream) {
   using C = BwdCfg<D, DV>;
@@ -764,15 +711,17 @@ static hipError_t launch_bwd_bf16(BwdParams p, const AttnArgs& a, hipStream_t st
 }
 
 template <int D>
-static hipError_t launch_bwd_f32(BwdParams p, hipStream_t stream) {
+static hipError_t launch_bwd_f32(BwdParams p, const AttnArgs& a, hipStream_t stream) {
   p.nqb = (p.Nq + 31) / 32;
+  // delta and the base-2 LSE, then the query-major dQ pass (no atomics),
+  // then dK and dV
   hipError_t e = launch_pre<D, float>(p, stream);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_dq(a, stream);
   if (e != hipSuccess) return e;
   const long long grid = (long long)p.B * p.H * p.nkb;
   hipLaunchKernelGGL(bwd_f32_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_convert<float>(p, D, stream);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- sink gradient
@@ -873,7 +822,6 @@ static hipError_t launch_bwd_main(const AttnArgs& a, hipStream_t stream) {
   p.uts = a.mask.uts;
   p.ute = a.mask.ute;
   p.table = a.table;
-  p.dq_acc = a.dq_acc;
   p.delta = a.delta;
   p.lse2 = a.lse2;
   p.dq = a.dq;
@@ -901,8 +849,8 @@ static hipError_t launch_bwd_main(const AttnArgs& a, hipStream_t stream) {
     if (a.d == 192 && a.dv == 128) return launch_bwd_bf16<192, 128>(p, a, stream);
   } else {
     switch (a.d) {
-      case 64: return launch_bwd_f32<64>(p, stream);
-      case 128: return launch_bwd_f32<128>(p, stream);
+      case 64: return launch_bwd_f32<64>(p, a, stream);
+      case 128: return launch_bwd_f32<128>(p, a, stream);
     }
   }
   return hipErrorInvalidValue;

@@ -749,6 +749,119 @@ static hipError_t launch_qmajor(FwdParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- fp32 dQ pass
+// The fp32 backward's dQ without atomics: query-major like the fp32
+// forward, 4 waves x 32 rows per workgroup. Each lane holds its row of Q and
+// dO as MFMA B operands; per visible 64-key tile, K and V go to LDS, then
+//   S^T = K Q^T and dP^T = V dO^T (masked like the forward),
+//   P = exp2(S * scale * log2e - LSE2), dS = P (dP - delta),
+//   dQ^T += K^T dS^T,
+// with LSE2 and delta from the preprocess. dQ sums in registers over the keys
+// in a fixed order and is written once: bitwise deterministic.
+template <int D>
+__global__ __launch_bounds__(256) void dq_f32_kernel(FwdParams p) {
+  constexpr int BC = 64, BR = 128, KS = D + 1, VS = D + 4;
+  __shared__ float ks[BC * KS];
+  __shared__ float vs[BC * VS];
+  __shared__ int vl[4 * 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int hh = lane >> 5;
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;
+  const int qb = p.nqb - 1 - (int)(blockIdx.x / BH);
+  const int b = bh / p.H, h = bh % p.H;
+  const int hmi = p.hm == 1 ? 0 : h;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const long long qslice = (long long)bh * Nq, kslice = (long long)bh * Nk;
+  const int r0 = qb * BR, r1 = min(Nq, r0 + BR);
+  const int i = r0 + 32 * w + (lane & 31);
+  const float* qg = reinterpret_cast<const float*>(p.q) + qslice * D;
+  const float* kg = reinterpret_cast<const float*>(p.k) + kslice * D;
+  const float* vg = reinterpret_cast<const float*>(p.v) + kslice * D;
+  const float* dog = reinterpret_cast<const float*>(p.dout) + qslice * D;
+  const long long vrow = ((long long)b * p.hm + hmi) * Nk;
+  const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb * 8;
+
+  float qf[D / 2], dof[D / 2];
+#pragma unroll
+  for (int t = 0; t < D / 2; ++t) {
+    qf[t] = i < Nq ? qg[(long long)i * D + 2 * t + hh] : 0.f;
+    dof[t] = i < Nq ? dog[(long long)i * D + 2 * t + hh] : 0.f;
+  }
+  // a row past Nq gets LSE2 = +inf, so its P (and dQ, not stored) is 0
+  const float lse2 = i < Nq ? p.lse2[qslice + i] : __builtin_inff();
+  const float delta = i < Nq ? p.delta[qslice + i] : 0.f;
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) dq[mb] = f32x16{};
+
+  for (int kb = 0; kb < p.nkb; ++kb) {
+    const BlockBounds bb = load_bounds(table + (long long)kb * 8);
+    const int c0 = kb * BC, c1 = min(Nk, c0 + BC);
+    const int wgc = tile_class(bb, r0, r1, c0, c1, p.causal != 0);
+    if (wgc == 0) continue;
+    int wc = 0;
+    const int a0 = r0 + 32 * w;
+    if (a0 < Nq) {
+      wc = tile_class(bb, a0, min(Nq, a0 + 32), c0, c1, p.causal != 0);
+      if (c1 - c0 < BC && wc == 2) wc = 1;
+    }
+    __syncthreads();
+    for (int t = tid; t < BC * D; t += 256) {
+      const int row = t / D, col = t % D;
+      const bool ok = c0 + row < Nk;
+      ks[row * KS + col] = ok ? kg[(long long)(c0 + row) * D + col] : 0.f;
+      vs[row * VS + col] = ok ? vg[(long long)(c0 + row) * D + col] : 0.f;
+    }
+    {
+      const int vsel = tid >> 6, kk = tid & 63;
+      const int32_t* src = vsel == 0 ? p.lts : vsel == 1 ? p.lte : vsel == 2 ? p.uts : p.ute;
+      const bool present = src != nullptr && (vsel < 2 ? p.has_lt : p.has_ut);
+      vl[vsel * 64 + kk] = (present && c0 + kk < Nk) ? src[vrow + c0 + kk] : 0;
+    }
+    __syncthreads();
+    if (wc == 0) continue;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const int row = jb * 32 + (lane & 31);
+#pragma unroll
+      for (int t = 0; t < D / 2; ++t) {
+        s = mfma32f(ks[row * KS + 2 * t + hh], qf[t], s);
+        dp = mfma32f(vs[row * VS + 2 * t + hh], dof[t], dp);
+      }
+      if (wc == 1) mask_block(s, (const FM_LDS int*)vl, jb * 32, c0, i, p, hh);
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = exp2f(__builtin_fmaf(s[r], p.sl2, -lse2)) * (dp[r] - delta);
+      // dQ^T += K^T dS^T over the block's 32 keys
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int key = jb * 32 + 8 * (t / 4) + 4 * hh + (t % 4);
+          dq[mb] = mfma32f(ks[key * KS + 32 * mb + (lane & 31)], ds[t], dq[mb]);
+        }
+    }
+  }
+
+  if (i < Nq) {
+    float* dqg = reinterpret_cast<float*>(p.dq) + (qslice + i) * D;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = dq[mb][4 * g + e] * p.scale;
+        *reinterpret_cast<f32x4*>(dqg + 32 * mb + 8 * g + 4 * hh) = v4;
+      }
+  }
+}
+
 // the bf16 (d, dv) pairs compiled in (kept in step with bf16_dims())
 template <int MODE>
 static hipError_t dispatch_qmajor(int d, int dv, const FwdParams& p, hipStream_t stream) {
@@ -837,6 +950,17 @@ hipError_t launch_bwd_dq(const AttnArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.sl2 = a.scale * kLog2e;
   p.nkb = (a.Nk + kFwdBlockK - 1) / kFwdBlockK;
+  if (!a.is_bf16) {
+    // fp32: delta and the base-2 LSE come from the preprocess, already run
+    p.nqb = (p.Nq + 127) / 128;
+    const long long grid = (long long)p.B * p.H * p.nqb;
+    switch (a.d) {
+      case 64: hipLaunchKernelGGL(dq_f32_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, p); break;
+      case 128: hipLaunchKernelGGL(dq_f32_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   return dispatch_qmajor<kModeDq>(a.d, a.dv, p, stream);
 }
 

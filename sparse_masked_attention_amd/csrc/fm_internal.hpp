@@ -50,7 +50,6 @@ struct AttnArgs {
   void* dq;
   void* dk;
   void* dv_out;
-  float* dq_acc;      // backward workspace (fp32 path): float32 [B, H, N, d]
   float* delta;       // backward workspace: float32 [B, H, N]
   float* lse2;        // backward workspace: float32 [B, H, N], base-2 logsumexp
   const float* sink;  // per-head sink logits [H] or nullptr

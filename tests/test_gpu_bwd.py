@@ -113,6 +113,19 @@ def test_bf16_backward_is_deterministic():
         assert torch.equal(x, y)
 
 
+def test_fp32_backward_is_deterministic():
+    """The fp32 dQ comes from its own query-major pass (no atomics), so all
+    three gradients repeat bitwise."""
+    B, H, N, d = 1, 2, 700, 64
+    say("bwd fp32 determinism")
+    q, k, v, do = qkvo(B, H, N, d, 2750, bf16=False, with_do=True)
+    vec = I.stack_masks([I.make_mask("document", N, np.random.default_rng(5))])
+    a = run_case(q, k, v, do, vec, dtype=torch.float32)
+    b = run_case(q, k, v, do, vec, dtype=torch.float32)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 def test_fully_masked_rows():
     N = 400
     say("bwd empty rows")
