@@ -9,19 +9,24 @@
 //   dS = P * (dO V^T - delta), delta_i = sum_m dO[i][m] * O[i][m],
 //   dQ = scale * dS K, dK = scale * dS^T Q.
 //
-// gfx950 mapping (bf16 path, d = dv in {64, 128}):
-//   * A workgroup (4 waves) owns 128 keys, 32 per wave; K and V of those keys
-//     stay in registers as MFMA operands, dK and dV accumulate in registers.
-//   * It walks the query blocks (64 rows) the mask leaves visible, found by
-//     the same per-block min/max classification as the forward, with a
-//     per-wave class so a wave whose 32 keys are hidden does no math.
+// Two passes, no atomics (every gradient sums in a fixed order, so the
+// results repeat bitwise):
+//   * dQ pass, query-major (fm_fwd.hip: qmajor_bf16_kernel in its dQ mode,
+//     dq_f32_kernel for fp32): each workgroup owns query rows, walks their
+//     visible key tiles and sums dQ in registers. The bf16 pass also forms
+//     delta and the base-2 LSE; for fp32 bwd_pre_kernel does.
+//   * dK/dV pass, key-major (this file): a workgroup (4 waves) owns 128 keys,
+//     32 per wave; K and V of those keys stay in registers as MFMA operands,
+//     dK and dV accumulate in registers.
+// gfx950 mapping of the bf16 dK/dV pass:
+//   * It walks the query blocks (64 rows; 32 at d > 128) the mask leaves
+//     visible, found by the same per-block min/max classification as the
+//     forward, with a per-wave class so a wave whose 32 keys are hidden does
+//     no math.
 //   * Q and dO tiles (plus LSE and delta) arrive by buffer loads straight into
 //     LDS, double buffered. P and dS are formed in the S = Q K^T accumulator
 //     layout, which is directly the A operand of dV += P^T dO and
 //     dK += dS^T Q; the Q/dO operands come from ds_read_b64_tr_b16.
-//   * dS^T goes to LDS once per step; each wave then forms a quarter of the
-//     step's dQ (64 rows x d) over all 128 keys and adds it into a float32
-//     accumulator with global atomics. A last kernel converts it to bf16.
 //   * Because each lane owns one key, the element mask test of a partial tile
 //     uses four per-lane registers (that key's bounds) and no memory.
 #include <type_traits>
