@@ -103,7 +103,8 @@ size_t flashmask_workspace_size_qk(int is_bwd, int B, int H, int Nq, int Nk, int
   if (!supported(d, dv, dtype)) return 0;
   size_t bytes = align_up(table_bytes(B, hm, Nk));
   if (is_bwd) {
-    bytes += 2 * align_up((size_t)B * H * Nq * sizeof(float));             // delta, base-2 LSE
+    // delta, base-2 LSE, rowsum(dS)
+    bytes += 3 * align_up((size_t)B * H * Nq * sizeof(float));
   }
   return bytes;
 }
@@ -244,6 +245,8 @@ fm_status_t flashmask_bwd_qk(const void* q, const void* k, const void* v, const 
   a.delta = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)B * H * Nq * sizeof(float));
   a.lse2 = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)B * H * Nq * sizeof(float));
+  a.pdsum = reinterpret_cast<float*>(ws);
   a.q = q;
   a.k = k;
   a.v = v;

@@ -730,14 +730,20 @@ static hipError_t launch_bwd_f32(BwdParams p, const AttnArgs& a, hipStream_t str
 }
 
 // ---------------------------------------------------------------- sink gradient
-// d loss / d s_h = -sum over the head's rows of exp(s_h - LSE_i) * delta_i:
-// the sink is one more softmax entry with a zero value vector, so its share
-// of row i is exp(s_h - LSE_i) and d O_i / d s_h = -that share * O_i. One
-// workgroup per head, a fixed summation order (per-thread strides, then
-// wave shuffles, then the 4 waves in order): deterministic. `have_rows` is
-// false when no row saw a key (then every O_i, and so every term, is 0).
+// d loss / d s_h = -sum over the head's rows of p_i * D_i, with p_i =
+// exp(s_h - LSE_i) the sink's share of row i (the sink is one more softmax
+// entry with a zero value vector, so d O_i / d s_h = -p_i * O_i) and
+// D_i = rowsum(P * dP)_i = dO_i . O_i. D_i is not taken from the bf16 O:
+// this sum over every row would collect O's rounding. Instead
+// D_i = rowsum(dS)_i + delta_i * (1 - p_i), which equals it exactly because
+// dS = P (dP - delta) and the row of P sums to 1 - p_i; rowsum(dS) comes from
+// the dQ pass, where the delta error cancels. One workgroup per head, a
+// fixed summation order (per-thread strides, then wave shuffles, then the 4
+// waves in order): deterministic. `have_rows` is false when no row saw a key
+// (then every O_i, and so every term, is 0).
 __global__ __launch_bounds__(256) void sink_grad_kernel(const float* __restrict__ lse2,
                                                         const float* __restrict__ delta,
+                                                        const float* __restrict__ dssum,
                                                         const float* __restrict__ sink,
                                                         float* __restrict__ dsink, int B, int H,
                                                         int Nq, int have_rows) {
@@ -747,7 +753,10 @@ __global__ __launch_bounds__(256) void sink_grad_kernel(const float* __restrict_
   if (have_rows) {
     for (int b = 0; b < B; ++b) {
       const long long base = ((long long)b * H + h) * Nq;
-      for (int i = threadIdx.x; i < Nq; i += 256) acc += exp2f(s2 - lse2[base + i]) * delta[base + i];
+      for (int i = threadIdx.x; i < Nq; i += 256) {
+        const float pi = exp2f(s2 - lse2[base + i]);
+        acc += pi * (dssum[base + i] + delta[base + i] * (1.f - pi));
+      }
     }
   }
 #pragma unroll
@@ -760,7 +769,7 @@ __global__ __launch_bounds__(256) void sink_grad_kernel(const float* __restrict_
 
 static hipError_t launch_sink_grad(const AttnArgs& a, bool have_rows, hipStream_t stream) {
   if (a.sink == nullptr || a.dsink == nullptr || a.H == 0) return hipSuccess;
-  hipLaunchKernelGGL(sink_grad_kernel, dim3((unsigned)a.H), dim3(256), 0, stream, a.lse2, a.delta,
+  hipLaunchKernelGGL(sink_grad_kernel, dim3((unsigned)a.H), dim3(256), 0, stream, a.lse2, a.delta, a.pdsum,
                      a.sink, a.dsink, a.B, a.H, a.Nq, have_rows ? 1 : 0);
   return hipGetLastError();
 }

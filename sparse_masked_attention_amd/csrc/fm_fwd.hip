@@ -40,6 +40,7 @@ struct FwdParams {
   void* o;
   float* lse;
   const float* sink;     // forward: per-head sink logits [H], or nullptr
+  float* pdsum;          // dQ passes with a sink: rowsum(dS) per row, [B, H, Nq]
   unsigned long long* counts;
   // dQ mode (backward): dO and the forward's O and natural-log LSE in; dQ
   // out, and per row the base-2 LSE and delta = rowsum(dO * O) out for the
@@ -121,6 +122,8 @@ __device__ inline void finish_row(float lt, float m, float scale, float s, bool 
 // transposed score layout S^T = K Q^T).
 constexpr int kModeFwd = 0;
 constexpr int kModeDq = 1;
+// dQ pass that also sums rowsum(dS) per row (for the sink gradient)
+constexpr int kModeDqSink = 2;
 
 // D: head dim of Q and K; DV: head dim of V (and O, dO).
 template <int D, int DV, int MODE>
@@ -130,7 +133,7 @@ struct QCfg {
   static constexpr int BR = WR * NW;                      // query rows per workgroup
   static constexpr int BC = 64;                           // keys per tile
   // 32-key blocks per inner step (1 keeps registers within budget)
-  static constexpr int JBS = (D > 128 || DV > 128 || MODE == kModeDq) ? 1 : 2;
+  static constexpr int JBS = (D > 128 || DV > 128 || MODE != kModeFwd) ? 1 : 2;
   // Forward with one wave per SIMD and room for both halves' scores (d = 192,
   // dv = 128): pipeline the tile's two 32-key halves within the wave. With
   // two waves per SIMD (d <= 128) the other wave already fills the MFMA pipe
@@ -170,7 +173,8 @@ constexpr float kRescaleSlack = 8.0f;
 template <int D, int DV, int MODE>
 __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf16_kernel(FwdParams p) {
   using C = QCfg<D, DV, MODE>;
-  constexpr bool DQ = MODE == kModeDq;
+  constexpr bool DQ = MODE != kModeFwd;
+  constexpr bool PD = MODE == kModeDqSink;
   // Two pipeline stages as separate LDS objects.
   __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
@@ -222,6 +226,7 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
     qf[c] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)(i * D + 16 * c + 8 * hh) * 2));
   bf16x8 dof[DQ ? DV / 16 : 1];
   float row_lse2 = 0.f, row_delta = 0.f;
+  float row_pd = 0.f;   // this lane's part of rowsum(dS) (kModeDqSink)
   if constexpr (DQ) {
     const __amdgpu_buffer_rsrc_t rdo =
         make_rsrc(reinterpret_cast<const bf16*>(p.dout) + qslice * DV, obytes);
@@ -373,7 +378,9 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pv = fast_exp2(__builtin_fmaf(s[r], p.sl2, -row_lse2));
-          pf[r / 8][r % 8] = (bf16)(pv * (dp[r] - row_delta));
+          const float dsv = pv * (dp[r] - row_delta);
+          pf[r / 8][r % 8] = (bf16)dsv;
+          if constexpr (PD) row_pd += dsv;   // the sink gradient's row sum of dS, in fp32
         }
         // dQ^T += K^T dS^T over the half's keys
 #pragma unroll
@@ -577,6 +584,11 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
     if (i < Nq && hh == 0) p.lse[qslice + i] = row_lse;
   } else {
     mul = p.scale;   // dQ = scale * dS K
+    if constexpr (PD) {
+      // rowsum(dS) for the sink gradient (see sink_grad_kernel)
+      const float pd = sum_x32(row_pd);
+      if (i < Nq && hh == 0) p.pdsum[qslice + i] = pd;
+    }
   }
   FM_LDS char* ost = (FM_LDS char*)(w < 2 ? stage0 : stage1) + (w & 1) * 32 * W * 2;
   // row r, chunk c at r * W * 2 + 16 (c ^ (r & 7)): rows spread over the banks
@@ -797,6 +809,7 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(FwdParams p) {
   f32x16 dq[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) dq[mb] = f32x16{};
+  float pd = 0.f;   // this lane's part of rowsum(dS), for the sink gradient
 
   for (int kb = 0; kb < p.nkb; ++kb) {
     const BlockBounds bb = load_bounds(table + (long long)kb * 8);
@@ -836,7 +849,10 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(FwdParams p) {
       if (wc == 1) mask_block(s, (const FM_LDS int*)vl, jb * 32, c0, i, p, hh);
       f32x16 ds;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ds[r] = exp2f(__builtin_fmaf(s[r], p.sl2, -lse2)) * (dp[r] - delta);
+      for (int r = 0; r < 16; ++r) {
+        ds[r] = exp2f(__builtin_fmaf(s[r], p.sl2, -lse2)) * (dp[r] - delta);
+        pd += ds[r];
+      }
       // dQ^T += K^T dS^T over the block's 32 keys
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb)
@@ -848,6 +864,8 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(FwdParams p) {
     }
   }
 
+  pd = sum_x32(pd);
+  if (p.pdsum != nullptr && i < Nq && hh == 0) p.pdsum[qslice + i] = pd;
   if (i < Nq) {
     float* dqg = reinterpret_cast<float*>(p.dq) + (qslice + i) * D;
 #pragma unroll
@@ -952,6 +970,7 @@ hipError_t launch_bwd_dq(const AttnArgs& a, hipStream_t stream) {
   p.nkb = (a.Nk + kFwdBlockK - 1) / kFwdBlockK;
   if (!a.is_bf16) {
     // fp32: delta and the base-2 LSE come from the preprocess, already run
+    p.pdsum = a.sink != nullptr ? a.pdsum : nullptr;
     p.nqb = (p.Nq + 127) / 128;
     const long long grid = (long long)p.B * p.H * p.nqb;
     switch (a.d) {
@@ -960,6 +979,10 @@ hipError_t launch_bwd_dq(const AttnArgs& a, hipStream_t stream) {
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+  }
+  if (a.sink != nullptr) {
+    p.pdsum = a.pdsum;
+    return dispatch_qmajor<kModeDqSink>(a.d, a.dv, p, stream);
   }
   return dispatch_qmajor<kModeDq>(a.d, a.dv, p, stream);
 }

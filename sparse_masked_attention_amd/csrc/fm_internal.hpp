@@ -52,6 +52,7 @@ struct AttnArgs {
   void* dv_out;
   float* delta;       // backward workspace: float32 [B, H, N]
   float* lse2;        // backward workspace: float32 [B, H, N], base-2 logsumexp
+  float* pdsum;       // backward workspace: float32 [B, H, Nq], rowsum(dS) (sink gradient)
   const float* sink;  // per-head sink logits [H] or nullptr
   float* dsink;       // backward: d loss / d sink [H] or nullptr
   unsigned long long* tile_counts;
