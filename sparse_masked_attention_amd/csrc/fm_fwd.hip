@@ -320,6 +320,7 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
     const FM_LDS char* vst = kst + C::KT;
     const FM_LDS int* vl = (const FM_LDS int*)(kst + C::KT + C::VT);
     constexpr int JBS = C::JBS;
+    constexpr int FPF = 3;   // operand ring depth of the forward S and PV products
     if (wc == 1) {
       // one key per lane: which of this wave's 32 rows the mask hides for it
       // (absent vectors were staged as zeros, and has_* gates their use)
@@ -449,12 +450,26 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
       f32x16 s[JBS];
 #pragma unroll
       for (int jj = 0; jj < JBS; ++jj) bias(s[jj], hk * JBS + jj);
-      // S^T = K Q^T
+      // S^T = K Q^T: the JBS accumulation chains alternate, and each K
+      // operand is read FPF MFMAs ahead through a ring of registers. A fence
+      // per step keeps reads and MFMAs in that order (the scheduler, short of
+      // registers, otherwise sinks each read to its MFMA and every MFMA waits
+      // out an LDS latency); VALU, SALU and transcendental work may cross it.
+      {
+        constexpr int NS = JBS * (D / 16);
+        auto rd = [&](int t) {
+          return row_read(KW{}, kst, (hk * JBS + t % JBS) * 32 + l32, 2 * (t / JBS) + hh);
+        };
+        bf16x8 ring[FPF];
 #pragma unroll
-      for (int jj = 0; jj < JBS; ++jj) {
-        const int row = (hk * JBS + jj) * 32 + l32;
+        for (int t = 0; t < FPF; ++t) ring[t] = rd(t);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) s[jj] = mfma32(row_read(KW{}, kst, row, 2 * c + hh), qf[c], s[jj]);
+        for (int t = 0; t < NS; ++t) {
+          const bf16x8 a = ring[t % FPF];
+          if (t + FPF < NS) ring[t % FPF] = rd(t + FPF);
+          s[t % JBS] = mfma32(a, qf[t / JBS], s[t % JBS]);
+          __builtin_amdgcn_sched_barrier(0x406);
+        }
       }
       bf16x8 pf[2 * JBS];
       float mx = max_acc(s);
@@ -481,12 +496,20 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
 #pragma unroll
       for (int c = 0; c < 2 * JBS; ++c) rs = sum8_bf16(pf[c], rs);
       l_run = rs;
-      // O^T += V^T P^T
+      // O^T += V^T P^T, V operands through the same kind of ring
+      {
+        constexpr int NMB = DV / 32, NPV = 2 * JBS * NMB;
+        auto rd = [&](int t) { return tr_read(VW{}, vst, 2 * JBS * hk + t / NMB, t % NMB); };
+        bf16x8 ring[FPF];
 #pragma unroll
-      for (int cc = 0; cc < 2 * JBS; ++cc) {
-        const int c = 2 * JBS * hk + cc;
+        for (int t = 0; t < FPF; ++t) ring[t] = rd(t);
 #pragma unroll
-        for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] = mfma32(tr_read(VW{}, vst, c, mb), pf[cc], oacc[mb]);
+        for (int t = 0; t < NPV; ++t) {
+          const bf16x8 a = ring[t % FPF];
+          if (t + FPF < NPV) ring[t % FPF] = rd(t + FPF);
+          oacc[t % NMB] = mfma32(a, pf[t / NMB], oacc[t % NMB]);
+          __builtin_amdgcn_sched_barrier(0x406);
+        }
       }
     }
     }
