@@ -355,8 +355,8 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
         const int row = jb * 32 + l32;
         // S^T = K Q^T + bias, dP^T = V dO^T. The two chains alternate while
         // both have steps left, and the K / V operands are read PF MFMAs
-        // ahead through a ring of registers (at two waves per SIMD a deeper
-        // ring, or fencing the order, spills registers).
+        // ahead through a ring of registers (a deeper ring spills at two
+        // waves per SIMD), with a fence per step holding that order.
         constexpr int PF = 2;
         constexpr int NS = D / 16, NP = DV / 16, NSP = NS + NP, NMIN = NS < NP ? NS : NP;
         auto is_s = [](int t) { return t < 2 * NMIN ? (t & 1) == 0 : NS > NP; };
@@ -373,6 +373,7 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
           if (t + PF < NSP) ring[t % PF] = rd(t + PF);
           if (is_s(t)) s = mfma32(a, qf[chunk(t)], s);
           else dp = mfma32(a, dof[chunk(t)], dp);
+          __builtin_amdgcn_sched_barrier(0x406);
         }
         // dS = P (dP - delta) with P = exp2(S * scale * log2e - LSE2)
         bf16x8 pf[2];
