@@ -149,6 +149,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D, DV>;
   __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage2[C::STAGE];
   __shared__ int list[C::LIST];
   __shared__ int wsum[C::NW];
   __shared__ unsigned wcount[3];
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   auto issue = [&](unsigned entry, auto stage_c) {
     constexpr int S = decltype(stage_c)::value;
-    FM_LDS char* st = (FM_LDS char*)(S ? stage1 : stage0);
+    FM_LDS char* st = (FM_LDS char*)(S == 0 ? stage0 : S == 1 ? stage1 : stage2);
     const int q0 = (int)(entry & 0xFFFFFFu) * C::BQ;
 #pragma unroll
     for (int u = 0; u < C::LOADS_Q; ++u) {
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     constexpr int S = decltype(stage_c)::value;
     const int wc = (int)((entry >> (24 + 2 * w)) & 3u);
     if (wc == 0) return;
-    const FM_LDS char* qst = (const FM_LDS char*)(S ? stage1 : stage0);
+    const FM_LDS char* qst = (const FM_LDS char*)(S == 0 ? stage0 : S == 1 ? stage1 : stage2);
     const FM_LDS char* dost = qst + C::QT;
     const FM_LDS float* lse_l = (const FM_LDS float*)(qst + C::QT + C::OT);
     const FM_LDS float* del_l = lse_l + C::BQ;
@@ -454,32 +455,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     __syncthreads();
     cnt += add;
     if (cnt > C::LIST - 256 || base + 256 >= p.nqb) {
+      // Three stages: tile it + 2 loads into the stage tile it - 1 used, so
+      // one barrier per step covers both hazards (every wave's loads of tile
+      // it have landed; no wave still reads the stage being refilled), and
+      // each tile's loads have two steps to arrive.
       auto step = [&](int it, auto stage_c) {
         constexpr int S = decltype(stage_c)::value;
         // uniform across the wave: keeps the class tests scalar branches
         const unsigned entry_it = uniform_u32((unsigned)list[it]);
         if (it + 1 < cnt) {
-          issue((unsigned)list[it + 1], std::integral_constant<int, 1 - S>{});
-          // waves 0 and 1 issued one more load (LSE2 / delta)
+          // tile it + 1's loads may stay in flight (waves 0 and 1 issue one
+          // more load per tile, LSE2 / delta)
           if (w < 2) wait_vmcnt<C::LOADS_PER_STEP>();
           else wait_vmcnt<C::LOADS_PER_STEP - 1>();
         } else {
           wait_vmcnt<0>();
         }
         lds_barrier();
+        if (it + 2 < cnt) issue((unsigned)list[it + 2], std::integral_constant<int, (S + 2) % 3>{});
         compute(entry_it, stage_c);
-        lds_barrier();
       };
       if (cnt > 0) issue((unsigned)list[0], std::integral_constant<int, 0>{});
-      for (int it = 0; it < cnt; it += 2) {
+      if (cnt > 1) issue((unsigned)list[1], std::integral_constant<int, 1>{});
+      for (int it = 0; it < cnt; it += 3) {
         step(it, std::integral_constant<int, 0>{});
         if (it + 1 < cnt) step(it + 1, std::integral_constant<int, 1>{});
+        if (it + 2 < cnt) step(it + 2, std::integral_constant<int, 2>{});
       }
       cnt = 0;
     }
   }
 
   wait_vmcnt<0>();  // no load into LDS may still be in flight when the wave ends
+  __syncthreads();  // every wave is done with the stages (the epilogue reuses them)
   // --- write dK = scale * dS^T Q and dV for this wave's keys. A lane holds
   // one column of 16 keys, so stores straight from registers write 2 bytes
   // per lane. Where they fit, the rows go through LDS instead (the stage
