@@ -79,9 +79,9 @@ fm_status_t flashmask_tile_shape(int is_bwd, int d, fm_dtype_t dtype,
 /* Bytes of device workspace flashmask_fwd (is_bwd == 0) or flashmask_bwd
  * (is_bwd != 0) needs for these sizes; 0 on invalid sizes. The workspace
  * needs 256-byte alignment. It holds per-call state (the key-block table;
- * for the backward also delta, the base-2 logsumexp and the row sums of dS
- * the sink gradient uses), so calls that may run at the same time need
- * separate workspaces. */
+ * for the backward also delta, the base-2 logsumexp, the row sums of dS
+ * the sink gradient uses and the work-queue counters of the dK/dV pass), so
+ * calls that may run at the same time need separate workspaces. */
 size_t flashmask_workspace_size(int is_bwd, int B, int H, int N, int d, int dv,
                                 int hm, fm_dtype_t dtype);
 

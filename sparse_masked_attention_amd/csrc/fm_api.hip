@@ -103,8 +103,8 @@ size_t flashmask_workspace_size_qk(int is_bwd, int B, int H, int Nq, int Nk, int
   if (!supported(d, dv, dtype)) return 0;
   size_t bytes = align_up(table_bytes(B, hm, Nk));
   if (is_bwd) {
-    // delta, base-2 LSE, rowsum(dS)
-    bytes += 3 * align_up((size_t)B * H * Nq * sizeof(float));
+    // delta, base-2 LSE, rowsum(dS), the dK/dV pass's work-queue counters
+    bytes += 3 * align_up((size_t)B * H * Nq * sizeof(float)) + align_up(8 * sizeof(int));
   }
   return bytes;
 }
@@ -247,6 +247,8 @@ fm_status_t flashmask_bwd_qk(const void* q, const void* k, const void* v, const 
   a.lse2 = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)B * H * Nq * sizeof(float));
   a.pdsum = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)B * H * Nq * sizeof(float));
+  a.queue = reinterpret_cast<int*>(ws);
   a.q = q;
   a.k = k;
   a.v = v;

@@ -24,11 +24,15 @@
 //     forward, with a per-wave class so a wave whose 32 keys are hidden does
 //     no math.
 //   * Q and dO tiles (plus LSE and delta) arrive by buffer loads straight into
-//     LDS, double buffered. P and dS are formed in the S = Q K^T accumulator
+//     LDS, through three stages. P and dS are formed in the S = Q K^T accumulator
 //     layout, which is directly the A operand of dV += P^T dO and
 //     dK += dS^T Q; the Q/dO operands come from ds_read_b64_tr_b16.
 //   * Because each lane owns one key, the element mask test of a partial tile
 //     uses four per-lane registers (that key's bounds) and no memory.
+//   * Workgroups are persistent (one per CU, taking key blocks from per-XCD
+//     work queues) where the output rows can be staged through LDS: the next
+//     key block's scan, first tiles, K and V are under way before the
+//     finished block's dK and dV are stored.
 #include <type_traits>
 
 #include "fm_device.hpp"
@@ -54,10 +58,12 @@ struct BwdParams {
   void* dk;
   void* dv;
   unsigned long long* counts;
+  int* queue;        // persistent dK/dV pass: one work-queue counter per queue, zero at launch
   int B, H, Nq, Nk, hm, causal;   // Nq query rows, Nk keys
   int has_lt, has_lte, has_ut;
   float scale, sl2;
   int nqb, nkb, nkb64;
+  int nqueue, per_queue;
 };
 
 // ---------------------------------------------------------------- preprocess
@@ -126,6 +132,10 @@ struct BwdCfg {
   static constexpr int STAGE = QT + OT + 2 * BQ * 4;  // Q, dO, LSE2, delta
   static constexpr int LIST = 1024;
   static constexpr int LOADS_PER_STEP = LOADS_Q + LOADS_O + 1;   // waves 0/1 add LSE2 / delta
+  // Where a wave's 32 dK (and dV) rows fit a quarter of a stage, the rows go
+  // out staged through LDS and the workgroups are persistent.
+  static constexpr bool PERSIST = DO == DVO && NW * KW * DO * 2 <= STAGE;
+  static constexpr int NSTORE = DO / 16 + DVO / 16;   // 16-byte row stores per lane of dK and dV
 };
 
 // Chunk swizzle shared by row reads (32 rows, one chunk) and transposed reads
@@ -153,71 +163,116 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ int list[C::LIST];
   __shared__ int wsum[C::NW];
   __shared__ unsigned wcount[3];
+  __shared__ int next_item;
+  constexpr bool kPersist = C::PERSIST;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int w = uniform(tid >> 6);
-  const int hh = lane >> 5;
-  const int l32 = lane & 31;
+  // This lane's index, its half-wave and index in it. They are re-derived
+  // through an opaque copy before each pass over a tile list, so addresses
+  // computed from them are not hoisted out of the item loop, where they would
+  // hold registers through the scan and the epilogue as well.
+  int lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  auto refresh_lane = [&]() {
+    lane = opaque_v(tid) & 63;
+    hh = lane >> 5;
+    l32 = lane & 31;
+  };
   const int BH = p.B * p.H;
-  int bh, rest;                              // heavy (early) key blocks first
-  xcd_order((int)blockIdx.x, BH, p.nkb * C::NSPLIT, bh, rest);
-  const int kb = rest / C::NSPLIT;
-  const int sp = rest % C::NSPLIT;           // which output column half
-  const int col0 = sp * C::DO;               // first dK column of this workgroup
-  const int col0v = sp * C::DVO;             // first dV column
-  const int b = bh / p.H, h = bh % p.H;
-  const int hmi = p.hm == 1 ? 0 : h;
   const int Nq = p.Nq, Nk = p.Nk;
-  const long long qslice = (long long)bh * Nq;    // rows of Q, dO, LSE, delta
-  const long long kslice = (long long)bh * Nk;    // rows of K, V, dK, dV
-  const int c0 = kb * C::BKC;
-  const int c1 = min(Nk, c0 + C::BKC);
-  const int wc0 = c0 + C::KW * w;                // this wave's first key
-  const int j = wc0 + l32;                        // this lane's key
   const uint32_t qbytes = (uint32_t)Nq * D * 2;    // one head of Q
   const uint32_t kbytes = (uint32_t)Nk * D * 2;    // one head of K
   const uint32_t vbytes = (uint32_t)Nk * DV * 2;   // one head of V
   const uint32_t obytes = (uint32_t)Nq * DV * 2;   // one head of dO
-
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const bf16*>(p.q) + qslice * D, qbytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + kslice * D, kbytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + kslice * DV, vbytes);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const bf16*>(p.dout) + qslice * DV, obytes);
-  const __amdgpu_buffer_rsrc_t rlse = make_rsrc(p.lse2 + qslice, (uint32_t)Nq * 4);
-  const __amdgpu_buffer_rsrc_t rdel = make_rsrc(p.delta + qslice, (uint32_t)Nq * 4);
-
-  // K and V of this lane's key as the B operands of S = Q K^T and dP = dO V^T
-  bf16x8 kB[D / 16], vB[DV / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c)
-    kB[c] = __builtin_bit_cast(bf16x8, buffer_load16(rk, (uint32_t)(j * D + 16 * c + 8 * hh) * 2));
-#pragma unroll
-  for (int c = 0; c < DV / 16; ++c)
-    vB[c] = __builtin_bit_cast(bf16x8, buffer_load16(rv, (uint32_t)(j * DV + 16 * c + 8 * hh) * 2));
-  // this lane's key bounds (the element test needs nothing else)
-  const long long vrow = ((long long)b * p.hm + hmi) * Nk;
-  int k_lts = Nq, k_lte = Nq, k_uts = 0, k_ute = 0;   // empty intervals
-  if (j < Nk) {
-    if (p.has_lt) {
-      k_lts = p.lts[vrow + j];
-      k_lte = p.has_lte ? p.lte[vrow + j] : Nq;
-    }
-    if (p.has_ut) {
-      k_uts = p.uts[vrow + j];
-      k_ute = p.ute[vrow + j];
-    }
-  }
   const bool causal = p.causal != 0, has_lt = p.has_lt != 0, has_ut = p.has_ut != 0;
-
-  f32x16 dvacc[C::DVO / 32], dkacc[C::DO / 32];
-#pragma unroll
-  for (int mb = 0; mb < C::DVO / 32; ++mb) dvacc[mb] = f32x16{};
-#pragma unroll
-  for (int mb = 0; mb < C::DO / 32; ++mb) dkacc[mb] = f32x16{};
   if (tid < 3) wcount[tid] = 0;
   unsigned cnt0 = 0, cnt1 = 0, cnt2 = 0;
-  const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb64 * 8;
+
+  // --- work items: (head, 128-key block, dK/dV column half). Without
+  // persistence, workgroup t does item t. Persistent workgroups (one per CU)
+  // take items from work queues: queue qi holds the items t = n * nqueue + qi
+  // in the order n = 0, 1, ..., which with 8 queues keeps every item of a
+  // head on one XCD (workgroup g serves queue g % 8 and the hardware deals
+  // workgroups to the 8 XCDs in turn), heavy (early) key blocks first. Each
+  // workgroup takes its next item at the start of the current one, and ends
+  // when its queue is empty: every wave reaches the end.
+  const int qi = kPersist ? (int)blockIdx.x % p.nqueue : 0;
+  int item;
+  if constexpr (kPersist) {
+    if (tid == 0) next_item = atomicAdd(p.queue + qi, 1);
+    __syncthreads();
+    item = uniform(next_item);         // the same value in every lane and wave
+    if (item >= p.per_queue) return;
+  } else {
+    item = (int)blockIdx.x;
+  }
+
+  // per-item state
+  int bh, kb, sp, col0, col0v, c0, c1, wc0, j;
+  long long qslice, kslice;
+  __amdgpu_buffer_rsrc_t rq, rk, rv, rdo, rlse, rdel;
+  const int32_t* table;
+  bool tail, count_item;
+  int k_lts, k_lte, k_uts, k_ute;
+  auto setup = [&](int it) {
+    int rest;
+    xcd_order(kPersist ? it * p.nqueue + qi : it, BH, p.nkb * C::NSPLIT, bh, rest);
+    kb = rest / C::NSPLIT;
+    sp = rest % C::NSPLIT;                 // which output column half
+    col0 = sp * C::DO;                     // first dK column of this item
+    col0v = sp * C::DVO;                   // first dV column
+    count_item = sp == 0;                  // column halves share their tiles: count them once
+    const int b = bh / p.H, h = bh % p.H;
+    const int hmi = p.hm == 1 ? 0 : h;
+    qslice = (long long)bh * Nq;           // rows of Q, dO, LSE, delta
+    kslice = (long long)bh * Nk;           // rows of K, V, dK, dV
+    c0 = kb * C::BKC;
+    c1 = min(Nk, c0 + C::BKC);
+    tail = c1 - c0 < C::BKC;
+    wc0 = c0 + C::KW * w;                  // this wave's first key
+    j = wc0 + l32;                         // this lane's key
+    rq = make_rsrc(reinterpret_cast<const bf16*>(p.q) + qslice * D, qbytes);
+    rk = make_rsrc(reinterpret_cast<const bf16*>(p.k) + kslice * D, kbytes);
+    rv = make_rsrc(reinterpret_cast<const bf16*>(p.v) + kslice * DV, vbytes);
+    rdo = make_rsrc(reinterpret_cast<const bf16*>(p.dout) + qslice * DV, obytes);
+    rlse = make_rsrc(p.lse2 + qslice, (uint32_t)Nq * 4);
+    rdel = make_rsrc(p.delta + qslice, (uint32_t)Nq * 4);
+    table = p.table + ((long long)b * p.hm + hmi) * p.nkb64 * 8;
+  };
+  // this lane's key bounds (the element test needs nothing else)
+  auto load_key_bounds = [&]() {
+    const int b = bh / p.H, h = bh % p.H;
+    const long long vrow = ((long long)b * p.hm + (p.hm == 1 ? 0 : h)) * Nk;
+    k_lts = Nq; k_lte = Nq; k_uts = 0; k_ute = 0;   // empty intervals
+    if (j < Nk) {
+      if (p.has_lt) {
+        k_lts = p.lts[vrow + j];
+        k_lte = p.has_lte ? p.lte[vrow + j] : Nq;
+      }
+      if (p.has_ut) {
+        k_uts = p.uts[vrow + j];
+        k_ute = p.ute[vrow + j];
+      }
+    }
+  };
+  // K and V of this lane's key as the B operands of S = Q K^T and dP = dO V^T
+  bf16x8 kB[D / 16], vB[DV / 16];
+  auto load_kv = [&]() {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      kB[c] = __builtin_bit_cast(bf16x8, buffer_load16(rk, (uint32_t)(j * D + 16 * c + 8 * hh) * 2));
+#pragma unroll
+    for (int c = 0; c < DV / 16; ++c)
+      vB[c] = __builtin_bit_cast(bf16x8, buffer_load16(rv, (uint32_t)(j * DV + 16 * c + 8 * hh) * 2));
+  };
+
+  f32x16 dvacc[C::DVO / 32], dkacc[C::DO / 32];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < C::DVO / 32; ++mb) dvacc[mb] = f32x16{};
+#pragma unroll
+    for (int mb = 0; mb < C::DO / 32; ++mb) dkacc[mb] = f32x16{};
+  };
 
   auto issue = [&](unsigned entry, auto stage_c) {
     constexpr int S = decltype(stage_c)::value;
@@ -391,78 +446,89 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // --- scan query blocks, compact the visible ones, process in chunks
-  const bool tail = c1 - c0 < C::BKC;
-  BlockBounds kbnd;
-  {
-    const BlockBounds a = load_bounds(table + (long long)(c0 / 64) * 8);
-    BlockBounds m = a;
-    if (c0 / 64 + 1 < p.nkb64) {
-      const BlockBounds q = load_bounds(table + (long long)(c0 / 64 + 1) * 8);
-      m.lts_mn = min(a.lts_mn, q.lts_mn); m.lts_mx = max(a.lts_mx, q.lts_mx);
-      m.lte_mn = min(a.lte_mn, q.lte_mn); m.lte_mx = max(a.lte_mx, q.lte_mx);
-      m.uts_mn = min(a.uts_mn, q.uts_mn); m.uts_mx = max(a.uts_mx, q.uts_mx);
-      m.ute_mn = min(a.ute_mn, q.ute_mn); m.ute_mx = max(a.ute_mx, q.ute_mx);
+
+  // --- scan the current item's query blocks from `base` on, compacting the
+  // visible ones into the list, until the list is nearly full or no block
+  // is left
+  int cnt = 0, base = 0;
+  auto scan = [&]() {
+    // bounds of keys c0 .. c0 + 63 (waves 0, 1), c0 + 64 .. c0 + 127 (waves
+    // 2, 3) and of both (read here, each time: kept across the tile loop
+    // they would only take registers)
+    static_assert(C::BKC == 128 && C::KW == 32, "two 64-key table entries per item, one per wave pair");
+    const BlockBounds kb_lo = load_bounds(table + (long long)(c0 / 64) * 8);
+    BlockBounds kb_hi = kb_lo, kbnd = kb_lo;
+    if (c0 / 64 + 1 < p.nkb64) {   // else keys c0 + 64 .. are past Nk
+      kb_hi = load_bounds(table + (long long)(c0 / 64 + 1) * 8);
+      kbnd.lts_mn = min(kb_lo.lts_mn, kb_hi.lts_mn); kbnd.lts_mx = max(kb_lo.lts_mx, kb_hi.lts_mx);
+      kbnd.lte_mn = min(kb_lo.lte_mn, kb_hi.lte_mn); kbnd.lte_mx = max(kb_lo.lte_mx, kb_hi.lte_mx);
+      kbnd.uts_mn = min(kb_lo.uts_mn, kb_hi.uts_mn); kbnd.uts_mx = max(kb_lo.uts_mx, kb_hi.uts_mx);
+      kbnd.ute_mn = min(kb_lo.ute_mn, kb_hi.ute_mn); kbnd.ute_mx = max(kb_lo.ute_mx, kb_hi.ute_mx);
     }
-    kbnd = m;
-  }
-  // K, V, the key bounds and the table entries are all needed before the
-  // first tile. Waiting for them here (the scan needs the table anyway) also
-  // tells the compiler nothing of its own is in flight inside the tile loop,
-  // where its waits would otherwise stall on the tile prefetch as well.
-  wait_vmcnt<0>();
-  int cnt = 0;
-  for (int base = 0; base < p.nqb; base += 256) {
-    const int qb = base + tid;
-    unsigned entry = 0;
-    bool valid = false;
-    if (qb < p.nqb) {
-      const int r0 = qb * C::BQ, r1 = min(Nq, r0 + C::BQ);
-      const int wgc = tile_class(kbnd, r0, r1, c0, c1, causal);
-      cnt0 += wgc == 0;
-      cnt1 += wgc == 1;
-      cnt2 += wgc == 2;
-      if (wgc != 0) {
-        valid = true;
-        const bool ragged = tail || (r1 - r0 < C::BQ);
-        int bits = 0;
-#pragma unroll
-        for (int ww = 0; ww < C::NW; ++ww) {
-          const int a0 = c0 + C::KW * ww;
-          int cls = 0;
-          if (a0 < Nk) {
-            const BlockBounds wb = load_bounds(table + (long long)(a0 / 64) * 8);
-            cls = tile_class(wb, r0, r1, a0, min(Nk, a0 + C::KW), causal);
-            if (ragged && cls == 2) cls = 1;
-          }
-          bits |= cls << (2 * ww);
+    cnt = 0;
+    do {
+      const int qb = base + tid;
+      unsigned entry = 0;
+      bool valid = false;
+      if (qb < p.nqb) {
+        const int r0 = qb * C::BQ, r1 = min(Nq, r0 + C::BQ);
+        const int wgc = tile_class(kbnd, r0, r1, c0, c1, causal);
+        if (count_item) {
+          cnt0 += wgc == 0;
+          cnt1 += wgc == 1;
+          cnt2 += wgc == 2;
         }
-        entry = (unsigned)qb | ((unsigned)bits << 24);
-      }
-    }
-    const unsigned long long bal = __ballot(valid);
-    const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
-    if (lane == 0) wsum[w] = __builtin_popcountll(bal);
-    __syncthreads();
-    int off = cnt, add = 0;
+        if (wgc != 0) {
+          valid = true;
+          const bool ragged = tail || (r1 - r0 < C::BQ);
+          int bits = 0;
 #pragma unroll
-    for (int ww = 0; ww < C::NW; ++ww) {
-      const int v = wsum[ww];
-      if (ww < w) off += v;
-      add += v;
-    }
-    if (valid) list[off + rank] = (int)entry;
-    __syncthreads();
-    cnt += add;
-    if (cnt > C::LIST - 256 || base + 256 >= p.nqb) {
-      // Three stages: tile it + 2 loads into the stage tile it - 1 used, so
-      // one barrier per step covers both hazards (every wave's loads of tile
-      // it have landed; no wave still reads the stage being refilled), and
-      // each tile's loads have two steps to arrive.
-      auto step = [&](int it, auto stage_c) {
-        constexpr int S = decltype(stage_c)::value;
-        // uniform across the wave: keeps the class tests scalar branches
-        const unsigned entry_it = uniform_u32((unsigned)list[it]);
+          for (int ww = 0; ww < C::NW; ++ww) {
+            const int a0 = c0 + C::KW * ww;
+            int cls = 0;
+            if (a0 < Nk) {
+              cls = tile_class(ww < 2 ? kb_lo : kb_hi, r0, r1, a0, min(Nk, a0 + C::KW), causal);
+              if (ragged && cls == 2) cls = 1;
+            }
+            bits |= cls << (2 * ww);
+          }
+          entry = (unsigned)qb | ((unsigned)bits << 24);
+        }
+      }
+      const unsigned long long bal = __ballot(valid);
+      const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+      if (lane == 0) wsum[w] = __builtin_popcountll(bal);
+      __syncthreads();
+      int off = cnt, add = 0;
+#pragma unroll
+      for (int ww = 0; ww < C::NW; ++ww) {
+        const int v = wsum[ww];
+        if (ww < w) off += v;
+        add += v;
+      }
+      if (valid) list[off + rank] = (int)entry;
+      __syncthreads();
+      cnt += uniform(add);   // the same in every lane: the loops over the list stay scalar
+      base += 256;
+    } while (cnt <= C::LIST - 256 && base < p.nqb);
+  };
+
+  // --- the list's tiles. Three stages: tile it + 2 loads into the stage tile
+  // it - 1 used, so one barrier per step covers both hazards (every wave's
+  // loads of tile it have landed; no wave still reads the stage being
+  // refilled), and each tile's loads have two steps to arrive. Steps below
+  // `skip` know their tile has landed already.
+  int skip = 0;
+  auto issue_first = [&]() {
+    if (cnt > 0) issue((unsigned)list[0], std::integral_constant<int, 0>{});
+    if (cnt > 1) issue((unsigned)list[1], std::integral_constant<int, 1>{});
+  };
+  auto run = [&]() {
+    auto step = [&](int it, auto stage_c) {
+      constexpr int S = decltype(stage_c)::value;
+      // uniform across the wave: keeps the class tests scalar branches
+      const unsigned entry_it = uniform_u32((unsigned)list[it]);
+      if (it >= skip) {
         if (it + 1 < cnt) {
           // tile it + 1's loads may stay in flight (waves 0 and 1 issue one
           // more load per tile, LSE2 / delta)
@@ -471,80 +537,147 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         } else {
           wait_vmcnt<0>();
         }
-        lds_barrier();
-        if (it + 2 < cnt) issue((unsigned)list[it + 2], std::integral_constant<int, (S + 2) % 3>{});
-        compute(entry_it, stage_c);
-      };
-      if (cnt > 0) issue((unsigned)list[0], std::integral_constant<int, 0>{});
-      if (cnt > 1) issue((unsigned)list[1], std::integral_constant<int, 1>{});
-      for (int it = 0; it < cnt; it += 3) {
-        step(it, std::integral_constant<int, 0>{});
-        if (it + 1 < cnt) step(it + 1, std::integral_constant<int, 1>{});
-        if (it + 2 < cnt) step(it + 2, std::integral_constant<int, 2>{});
       }
-      cnt = 0;
+      lds_barrier();
+      if (it + 2 < cnt) issue((unsigned)list[it + 2], std::integral_constant<int, (S + 2) % 3>{});
+      compute(entry_it, stage_c);
+    };
+    for (int it = 0; it < cnt; it += 3) {
+      step(it, std::integral_constant<int, 0>{});
+      if (it + 1 < cnt) step(it + 1, std::integral_constant<int, 1>{});
+      if (it + 2 < cnt) step(it + 2, std::integral_constant<int, 2>{});
     }
-  }
+  };
 
-  wait_vmcnt<0>();  // no load into LDS may still be in flight when the wave ends
-  __syncthreads();  // every wave is done with the stages (the epilogue reuses them)
-  // --- write dK = scale * dS^T Q and dV for this wave's keys. A lane holds
-  // one column of 16 keys, so stores straight from registers write 2 bytes
-  // per lane. Where they fit, the rows go through LDS instead (the stage
-  // buffers are free: every wave has passed its final barrier and no load
-  // into LDS is in flight) and each store writes whole rows, 16 bytes per
-  // lane: dK of the 4 waves in stage 0, dV in stage 1.
-  constexpr bool kStaged = 4 * 32 * C::DO * 2 <= C::STAGE && 4 * 32 * C::DVO * 2 <= C::STAGE;
-  if constexpr (kStaged) {
-    // key row kr, 16-byte chunk c of a W-wide row at kr * W * 2 + 16 (c ^ (kr & 7))
-    auto stage_rows = [&](FM_LDS char* base, const f32x16* acc, float mul, auto w_c) {
-      constexpr int W = decltype(w_c)::value;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = 8 * (r / 4) + 4 * hh + (r % 4);
-#pragma unroll
-        for (int mb = 0; mb < W / 32; ++mb) {
-          const int col = 32 * mb + l32;
-          *reinterpret_cast<FM_LDS bf16*>(base + kr * W * 2 + (((col >> 3) ^ (kr & 7)) << 4) + (col & 7) * 2) =
-              (bf16)(acc[mb][r] * mul);
-        }
-      }
-    };
-    auto store_rows = [&](const FM_LDS char* base, bf16* g, int ld, auto w_c) {
-      constexpr int W = decltype(w_c)::value;
-      constexpr int CH = W / 8;
-#pragma unroll
-      for (int k = 0; k < CH / 2; ++k) {
-        const int f = 64 * k + lane;
-        const int row = f / CH, c = f % CH;
-        const u32x4 val = *reinterpret_cast<const FM_LDS u32x4*>(base + row * W * 2 + ((c ^ (row & 7)) << 4));
-        if (wc0 + row < Nk) *reinterpret_cast<u32x4*>(g + (long long)(wc0 + row) * ld + 8 * c) = val;
-      }
-    };
-    FM_LDS char* kst = (FM_LDS char*)stage0 + w * 32 * C::DO * 2;
-    FM_LDS char* vst = (FM_LDS char*)stage1 + w * 32 * C::DVO * 2;
-    stage_rows(kst, dkacc, p.scale, std::integral_constant<int, C::DO>{});
-    stage_rows(vst, dvacc, 1.f, std::integral_constant<int, C::DVO>{});
-    __builtin_amdgcn_wave_barrier();
-    store_rows(kst, reinterpret_cast<bf16*>(p.dk) + kslice * D + col0, D, std::integral_constant<int, C::DO>{});
-    store_rows(vst, reinterpret_cast<bf16*>(p.dv) + kslice * DV + col0v, DV, std::integral_constant<int, C::DVO>{});
-  } else if (wc0 < Nk) {
-    bf16* dkg = reinterpret_cast<bf16*>(p.dk) + kslice * D;
-    bf16* dvg = reinterpret_cast<bf16*>(p.dv) + kslice * DV;
+  // key row kr, 16-byte chunk c of a W-wide staged row at kr * W * 2 + 16 (c ^ (kr & 7));
+  // eh, el32: this lane's half-wave and index in it
+  auto stage_rows = [&](FM_LDS char* st, const f32x16* acc, float mul, int eh, int el32, auto w_c) {
+    constexpr int W = decltype(w_c)::value;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = wc0 + 8 * (r / 4) + 4 * hh + (r % 4);
-      if (key < Nk) {
+      const int kr = 8 * (r / 4) + 4 * eh + (r % 4);
 #pragma unroll
-        for (int mb = 0; mb < C::DO / 32; ++mb)
-          dkg[(long long)key * D + col0 + 32 * mb + l32] = (bf16)(dkacc[mb][r] * p.scale);
-#pragma unroll
-        for (int mb = 0; mb < C::DVO / 32; ++mb)
-          dvg[(long long)key * DV + col0v + 32 * mb + l32] = (bf16)dvacc[mb][r];
+      for (int mb = 0; mb < W / 32; ++mb) {
+        const int col = 32 * mb + el32;
+        *reinterpret_cast<FM_LDS bf16*>(st + kr * W * 2 + (((col >> 3) ^ (kr & 7)) << 4) + (col & 7) * 2) =
+            (bf16)(acc[mb][r] * mul);
       }
     }
+  };
+
+  // --- first item: K and V, the key bounds and the table entries before the
+  // scan. The wait also tells the compiler that nothing of its own is in
+  // flight inside the tile loop, where its waits would otherwise stall on
+  // the tile prefetch as well (the loads into LDS are invisible to it).
+  setup(item);
+  load_kv();
+  load_key_bounds();
+  zero_acc();
+  wait_vmcnt<0>();
+  scan();
+  issue_first();
+  for (;;) {
+    refresh_lane();
+    run();
+    if (base < p.nqb) {   // more query blocks of this item
+      scan();
+      issue_first();
+      skip = 0;
+      continue;
+    }
+    if constexpr (!kPersist) {
+      // --- write dK = scale * dS^T Q and dV for this wave's keys straight
+      // from registers (a lane holds one column of 16 keys: 2 bytes per lane
+      // and store; the rows are too wide for the stages)
+      wait_vmcnt<0>();  // no load into LDS may still be in flight when the wave ends
+      if (wc0 < Nk) {
+        bf16* dkg = reinterpret_cast<bf16*>(p.dk) + kslice * D;
+        bf16* dvg = reinterpret_cast<bf16*>(p.dv) + kslice * DV;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = wc0 + 8 * (r / 4) + 4 * hh + (r % 4);
+          if (key < Nk) {
+#pragma unroll
+            for (int mb = 0; mb < C::DO / 32; ++mb)
+              dkg[(long long)key * D + col0 + 32 * mb + l32] = (bf16)(dkacc[mb][r] * p.scale);
+#pragma unroll
+            for (int mb = 0; mb < C::DVO / 32; ++mb)
+              dvg[(long long)key * DV + col0v + 32 * mb + l32] = (bf16)dvacc[mb][r];
+          }
+        }
+      }
+      break;
+    } else {
+      // --- the item is done. Its dK and dV rows (this wave's 32 keys) go out
+      // through buffer resources that end at the last key, so stores past Nk
+      // are dropped and every wave issues the same C::NSTORE stores.
+      const int nrow = uniform(max(0, min(C::KW, Nk - wc0)));
+      const __amdgpu_buffer_rsrc_t rdk =
+          make_rsrc(uniform_ptr(reinterpret_cast<bf16*>(p.dk) + (kslice + wc0) * D + col0),
+                    nrow > 0 ? (uint32_t)((nrow - 1) * D + C::DO) * 2 : 0u);
+      const __amdgpu_buffer_rsrc_t rdv =
+          make_rsrc(uniform_ptr(reinterpret_cast<bf16*>(p.dv) + (kslice + wc0) * DV + col0v),
+                    nrow > 0 ? (uint32_t)((nrow - 1) * DV + C::DVO) * 2 : 0u);
+      // the next item: its ticket is taken here (nothing else is in flight)
+      __syncthreads();   // no wave still reads this item's list, stages or the last ticket
+      if (tid == 0) next_item = atomicAdd(p.queue + qi, 1);
+      __syncthreads();
+      const int nitem = uniform(next_item);
+      const bool more = nitem < p.per_queue;   // the same in every wave
+      if (more) {
+        // Start the next item before this one's stores: its scan, its first
+        // two tiles (stages 0 and 1), then its K, V and key bounds. The
+        // stores below are then the last vector-memory operations in flight,
+        // and a wait that leaves just them outstanding finds all of this
+        // landed.
+        item = nitem;
+        setup(item);
+        base = 0;
+        scan();
+        issue_first();
+        load_kv();
+        load_key_bounds();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // dK = scale * dS^T Q, then dV, through this wave's quarter of stage 2
+      // (free: the next item's first tiles are in stages 0 and 1). A lane
+      // holds one column of 16 keys; staged, each store writes whole rows,
+      // 16 bytes per lane.
+      FM_LDS char* est = (FM_LDS char*)stage2 + w * C::KW * C::DO * 2;
+      // The lane index is re-derived here through an opaque copy: addresses
+      // computed from it cannot then be hoisted above the tile loop, where
+      // they would hold registers for the whole item.
+      const int elane = opaque_v(tid) & 63;
+      auto store_rows = [&](__amdgpu_buffer_rsrc_t r, int ld, auto w_c) {
+        constexpr int W = decltype(w_c)::value;
+        constexpr int CH = W / 8;
+#pragma unroll
+        for (int k = 0; k < CH / 2; ++k) {
+          const int f = 64 * k + elane;
+          const int row = f / CH, c = f % CH;
+          const u32x4 val = *reinterpret_cast<const FM_LDS u32x4*>(est + row * W * 2 + ((c ^ (row & 7)) << 4));
+          __builtin_amdgcn_raw_buffer_store_b128(val, r, (uint32_t)(row * ld + 8 * c) * 2, 0, 0);
+        }
+      };
+      stage_rows(est, dkacc, p.scale, elane >> 5, elane & 31, std::integral_constant<int, C::DO>{});
+      __builtin_amdgcn_wave_barrier();
+      store_rows(rdk, D, std::integral_constant<int, C::DO>{});
+      stage_rows(est, dvacc, 1.f, elane >> 5, elane & 31, std::integral_constant<int, C::DVO>{});
+      __builtin_amdgcn_wave_barrier();
+      store_rows(rdv, DV, std::integral_constant<int, C::DVO>{});
+      __builtin_amdgcn_sched_barrier(0);
+      // the next item's first two tiles, K, V and key bounds have landed;
+      // only the stores may be in flight. (Waited
+      // for on both paths, so that the compiler also sees K and V landed
+      // wherever the loop continues.)
+      wait_vmcnt<C::NSTORE>();
+      if (!more) break;
+      zero_acc();
+      skip = 2;
+    }
   }
-  if (p.counts != nullptr && sp == 0) {
+  wait_vmcnt<0>();
+  if (p.counts != nullptr) {
     atomicAdd(&wcount[0], cnt0);
     atomicAdd(&wcount[1], cnt1);
     atomicAdd(&wcount[2], cnt2);
@@ -711,6 +844,20 @@ static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// compute units of the current device (cached per device)
+static int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int D, int DV>
 static hipError_t launch_bwd_bf16(BwdParams p, const AttnArgs& a, hipStream_t stream) {
   using C = BwdCfg<D, DV>;
@@ -718,7 +865,20 @@ static hipError_t launch_bwd_bf16(BwdParams p, const AttnArgs& a, hipStream_t st
   // the dQ pass also writes delta and the base-2 LSE the dK/dV pass reads
   const hipError_t e = launch_bwd_dq(a, stream);
   if (e != hipSuccess) return e;
-  const long long grid = (long long)p.B * p.H * p.nkb * C::NSPLIT;
+  const long long items = (long long)p.B * p.H * p.nkb * C::NSPLIT;
+  long long grid = items;
+  if constexpr (C::PERSIST) {
+    // one workgroup per CU, 8 queues (one per XCD) when the heads split
+    // evenly over them; the dQ pass has zeroed the counters
+    if (a.queue == nullptr) return hipErrorInvalidValue;
+    p.queue = a.queue;
+    p.nqueue = (p.B * p.H) % 8 == 0 ? 8 : 1;
+    p.per_queue = (int)(items / p.nqueue);
+    const int ncu = cu_count();
+    if (ncu <= 0) return hipErrorInvalidDevice;
+    const long long slots = ncu >= p.nqueue ? ncu / p.nqueue * p.nqueue : p.nqueue;
+    grid = items < slots ? items : slots;
+  }
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, DV>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

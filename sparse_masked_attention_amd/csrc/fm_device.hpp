@@ -62,9 +62,25 @@ __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// A copy of x the compiler must treat as unknown: values computed from it
+// stay after this point instead of being hoisted out of enclosing loops.
+__device__ inline int opaque_v(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// a wave-uniform pointer the compiler also knows to be uniform (scalar registers)
+template <typename T>
+__device__ inline T* uniform_ptr(T* x) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32));
+  return reinterpret_cast<T*>(((unsigned long long)hi << 32) | lo);
+}
 
 // ---------------------------------------------------------------- LDS reads
 __device__ inline bf16x8 lds_read_b128(const FM_LDS void* p) {

@@ -51,6 +51,7 @@ struct FwdParams {
   float* lse2;
   float* delta;
   void* dq;
+  int* qzero;            // bf16 dQ pass: the dK/dV pass's 8 work-queue counters, zeroed here
   int B, H, Nq, Nk, hm, causal;   // Nq query rows, Nk keys
   int has_lt, has_lte, has_ut;
   float scale, sl2;
@@ -635,6 +636,11 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
     const u32x4 val = *reinterpret_cast<const FM_LDS u32x4*>(ost + row * W * 2 + ((c ^ (row & 7)) << 4));
     if (wr0 + row < Nq) *reinterpret_cast<u32x4*>(outg + (long long)row * W + 8 * c) = val;
   }
+  if constexpr (DQ) {
+    // the dK/dV pass that follows on this stream takes work from these
+    // counters (wave 0 of one workgroup: lane l zeroes counter l % 8)
+    if (p.qzero != nullptr && blockIdx.x == 0 && w == 0) p.qzero[lane & 7] = 0;
+  }
   if (p.counts != nullptr) {
     atomicAdd(&wcount[0], cnt0);
     atomicAdd(&wcount[1], cnt1);
@@ -1004,6 +1010,8 @@ hipError_t launch_bwd_dq(const AttnArgs& a, hipStream_t stream) {
     }
     return hipGetLastError();
   }
+  // the dK/dV pass that follows on this stream takes work from these counters
+  p.qzero = a.queue;
   if (a.sink != nullptr) {
     p.pdsum = a.pdsum;
     return dispatch_qmajor<kModeDqSink>(a.d, a.dv, p, stream);

@@ -53,6 +53,7 @@ struct AttnArgs {
   float* delta;       // backward workspace: float32 [B, H, N]
   float* lse2;        // backward workspace: float32 [B, H, N], base-2 logsumexp
   float* pdsum;       // backward workspace: float32 [B, H, Nq], rowsum(dS) (sink gradient)
+  int* queue;         // backward workspace: 8 work-queue counters of the bf16 dK/dV pass
   const float* sink;  // per-head sink logits [H] or nullptr
   float* dsink;       // backward: d loss / d sink [H] or nullptr
   unsigned long long* tile_counts;

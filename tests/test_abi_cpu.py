@@ -73,9 +73,10 @@ def test_workspace_size(lib):
     import torch
     fwd = _binding.workspace_size(False, 1, 32, 8192, 128, 128, 1, torch.bfloat16)
     assert fwd == 128 * 8 * 4              # the table: 128 key blocks x 8 int32
-    # table, then delta, base-2 LSE and rowsum(dS) (the sink gradient's), one float per row each
+    # table, then delta, base-2 LSE and rowsum(dS) (the sink gradient's), one
+    # float per row each, then the dK/dV pass's 8 work-queue counters (256 bytes)
     bwd = _binding.workspace_size(True, 1, 32, 8192, 128, 128, 1, torch.bfloat16)
-    assert bwd == 4096 + 3 * 32 * 8192 * 4
+    assert bwd == 4096 + 3 * 32 * 8192 * 4 + 256
     # fp32 the same: its dQ pass needs no accumulator
     bwd32 = _binding.workspace_size(True, 1, 32, 8192, 128, 128, 1, torch.float32)
     assert bwd32 == bwd
@@ -148,10 +149,10 @@ def test_binding_refuses_cpu_tensors(lib):
 
 def test_rectangular_workspace_and_empty_sides(lib):
     import torch
-    # table over Nk keys, delta and base-2 LSE over Nq rows
-    # 5 key blocks x 32 bytes -> 256; 3 x (1 x 2 x 100 floats) -> 3 x 1024
+    # table over Nk keys, delta, base-2 LSE and rowsum(dS) over Nq rows, queue counters
+    # 5 key blocks x 32 bytes -> 256; 3 x (1 x 2 x 100 floats) -> 3 x 1024; 8 ints -> 256
     assert _binding.workspace_size(True, 1, 2, 100, 128, 128, 1, torch.bfloat16, Nk=300) == \
-        256 + 3 * 1024
+        256 + 3 * 1024 + 256
     assert _binding.workspace_size(False, 1, 2, 100, 128, 128, 1, torch.bfloat16, Nk=0) == 0
     p = lambda x: None if x is None else ctypes.c_void_p(x * 256)
     fwd = lambda Nq, Nk, q=1: lib.flashmask_fwd_qk(p(q), p(1), p(1), p(1), None, None, None, 1, None,
