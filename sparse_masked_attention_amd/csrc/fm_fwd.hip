@@ -570,17 +570,13 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
         // uniform across the wave: keeps the class tests scalar branches
         const int kb_it = uniform(list[it]);
         const unsigned cls_it = uniform_u32(list_cls[it]);
-        if (it + 1 < cnt) {
-          issue(list[it + 1], std::integral_constant<int, 1 - S>{});
-          // waves 0-3 issued one more load (a boundary vector)
-          if (w < 4) wait_vmcnt<C::LOADS_PER_TILE>();
-          else wait_vmcnt<C::LOADS_PER_TILE - 1>();
-        } else {
-          wait_vmcnt<0>();
-        }
+        // Tile it is the only load in flight. Once every wave has it (the
+        // barrier), every wave is also done with tile it - 1, whose stage
+        // then takes tile it + 1: one barrier per tile.
+        wait_vmcnt<0>();
         lds_barrier();
+        if (it + 1 < cnt) issue(list[it + 1], std::integral_constant<int, 1 - S>{});
         compute(kb_it, cls_it, stage_c);
-        lds_barrier();
       };
       if (cnt > 0) issue(list[0], std::integral_constant<int, 0>{});
       for (int it = 0; it < cnt; it += 2) {
@@ -600,6 +596,7 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
   constexpr int W = DQ ? D : DV;   // output row width
   constexpr int CH = W / 8;        // 16-byte chunks per row
   static_assert(2 * 32 * W * 2 <= C::STAGE, "two waves' rows fit one stage");
+  __syncthreads();   // every wave is done with the stages
   float mul;
   if constexpr (!DQ) {
     // normalise, store O (bf16) and the natural-log LSE
