@@ -351,13 +351,14 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
       // latencies; holding both halves at once would need one per CU)
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
-        f32x16 s, dp = f32x16{};
-        bias(s, jb);
+        f32x16 s, dp;
         const int row = jb * 32 + l32;
         // S^T = K Q^T + bias, dP^T = V dO^T. The two chains alternate while
         // both have steps left, and the K / V operands are read PF MFMAs
         // ahead through a ring of registers (a deeper ring spills at two
-        // waves per SIMD), with a fence per step holding that order.
+        // waves per SIMD), with a fence per step holding that order. Written
+        // twice: a partial tile starts S at the mask's bias, a full one at
+        // zero, taken by the first MFMA as an inline constant.
         constexpr int PF = 2;
         constexpr int NS = D / 16, NP = DV / 16, NSP = NS + NP, NMIN = NS < NP ? NS : NP;
         auto is_s = [](int t) { return t < 2 * NMIN ? (t & 1) == 0 : NS > NP; };
@@ -365,16 +366,26 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
         auto rd = [&](int t) {
           return is_s(t) ? row_read(KW{}, kst, row, 2 * chunk(t) + hh) : row_read(VW{}, vst, row, 2 * chunk(t) + hh);
         };
-        bf16x8 ring[PF];
+        auto sdp_chain = [&](auto part_c) {
+          constexpr bool PART = decltype(part_c)::value;
+          if constexpr (PART) bias(s, jb);   // also right for a full tile (zero bias)
+          bf16x8 ring[PF];
 #pragma unroll
-        for (int t = 0; t < PF; ++t) ring[t] = rd(t);
+          for (int t = 0; t < PF; ++t) ring[t] = rd(t);
 #pragma unroll
-        for (int t = 0; t < NSP; ++t) {
-          const bf16x8 a = ring[t % PF];
-          if (t + PF < NSP) ring[t % PF] = rd(t + PF);
-          if (is_s(t)) s = mfma32(a, qf[chunk(t)], s);
-          else dp = mfma32(a, dof[chunk(t)], dp);
-          __builtin_amdgcn_sched_barrier(0x406);
+          for (int t = 0; t < NSP; ++t) {
+            const bf16x8 a = ring[t % PF];
+            if (t + PF < NSP) ring[t % PF] = rd(t + PF);
+            if (is_s(t)) s = mfma32(a, qf[chunk(t)], (!PART && chunk(t) == 0) ? f32x16{} : s);
+            else dp = mfma32(a, dof[chunk(t)], chunk(t) == 0 ? f32x16{} : dp);
+            __builtin_amdgcn_sched_barrier(0x406);
+          }
+        };
+        if constexpr (PD) {
+          sdp_chain(std::true_type{});   // one chain (two spill here: the dS row sum holds registers)
+        } else {
+          if (wc == 1) sdp_chain(std::true_type{});
+          else sdp_chain(std::false_type{});
         }
         // dS = P (dP - delta) with P = exp2(S * scale * log2e - LSE2)
         bf16x8 pf[2];
@@ -450,14 +461,20 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
 #pragma unroll
     for (int hk = 0; hk < C::BC / 32 / JBS; ++hk) {
       f32x16 s[JBS];
-#pragma unroll
-      for (int jj = 0; jj < JBS; ++jj) bias(s[jj], hk * JBS + jj);
       // S^T = K Q^T: the JBS accumulation chains alternate, and each K
       // operand is read FPF MFMAs ahead through a ring of registers. A fence
       // per step keeps reads and MFMAs in that order (the scheduler, short of
       // registers, otherwise sinks each read to its MFMA and every MFMA waits
       // out an LDS latency); VALU, SALU and transcendental work may cross it.
-      {
+      // Written twice: a partial tile starts the chains at the mask's bias,
+      // a full one at zero, which the first MFMA then takes as an inline
+      // constant (one shared start would cost a register move per element).
+      auto s_chain = [&](auto part_c) {
+        constexpr bool PART = decltype(part_c)::value;
+        if constexpr (PART) {   // (also right for a full tile: zero bias)
+#pragma unroll
+          for (int jj = 0; jj < JBS; ++jj) bias(s[jj], hk * JBS + jj);
+        }
         constexpr int NS = JBS * (D / 16);
         auto rd = [&](int t) {
           return row_read(KW{}, kst, (hk * JBS + t % JBS) * 32 + l32, 2 * (t / JBS) + hh);
@@ -469,9 +486,16 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
         for (int t = 0; t < NS; ++t) {
           const bf16x8 a = ring[t % FPF];
           if (t + FPF < NS) ring[t % FPF] = rd(t + FPF);
-          s[t % JBS] = mfma32(a, qf[t / JBS], s[t % JBS]);
+          if (!PART && t < JBS) s[t % JBS] = mfma32(a, qf[t / JBS], f32x16{});
+          else s[t % JBS] = mfma32(a, qf[t / JBS], s[t % JBS]);
           __builtin_amdgcn_sched_barrier(0x406);
         }
+      };
+      if constexpr (D > 128) {
+        s_chain(std::true_type{});   // one chain (two spill at d = 256)
+      } else {
+        if (wc == 1) s_chain(std::true_type{});
+        else s_chain(std::false_type{});
       }
       bf16x8 pf[2 * JBS];
       float mx = max_acc(s);
