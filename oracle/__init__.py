@@ -9,10 +9,11 @@ Pins (tests/test_oracle_pins.py): every function here is checked against
 something other than itself (textbook attention, finite differences, brute
 force, closed forms, hand-worked fixtures).
 """
-from .attention import dense_mask, mask_row, forward, forward_rows, backward, softmax_probs
+from .attention import (dense_mask, mask_row, forward, forward_rows, backward, backward_sampled,
+                        softmax_probs)
 from .tables import kblock_minmax, classify, classify_counts, nnz_dense
 from . import families
 
 __all__ = ["dense_mask", "mask_row", "forward", "forward_rows", "backward",
-           "softmax_probs", "kblock_minmax", "classify", "classify_counts",
+           "backward_sampled", "softmax_probs", "kblock_minmax", "classify", "classify_counts",
            "nnz_dense", "families"]

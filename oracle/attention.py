@@ -42,7 +42,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = ["dense_mask", "mask_row", "forward", "forward_rows", "backward",
-           "softmax_probs"]
+           "backward_sampled", "softmax_probs"]
 
 
 def mask_row(vec: Optional[np.ndarray], b: int, h: int) -> Optional[np.ndarray]:
@@ -197,4 +197,52 @@ def backward(q, k, v, do, causal, lts=None, lte=None, uts=None, ute=None,
             dsink[h] -= float((np.exp(s_h - lse) * D).sum())
     if sink is not None:
         return dq, dk, dvv, dsink
+    return dq, dk, dvv
+
+
+def backward_sampled(q, k, v, do, causal, lts=None, lte=None, uts=None, ute=None,
+                     rows=(), keys=(), scale=None, chunk: int = 1024):
+    """dQ at the given query rows and dK, dV at the given key columns of one
+    (batch, head), with the gradient formulas of ``backward``, for sequences
+    too long for its dense Nq x Nk matrices.
+
+    q [Nq, d], k [Nk, d], v [Nk, dv], do [Nq, dv]; vectors [Nk]. Every row
+    contributes to dK and dV, so all rows are evaluated, ``chunk`` rows at a
+    time (as in forward_rows). Within a chunk, a key column that is masked in
+    every row of the chunk has probability exactly 0 in all of them and is
+    left out of that chunk's softmax: the values are those over all columns.
+    Returns (dq [len(rows), d], dk [len(keys), d], dv [len(keys), dv]).
+    """
+    Q = np.asarray(q, np.float64)
+    K = np.asarray(k, np.float64)
+    V = np.asarray(v, np.float64)
+    dO = np.asarray(do, np.float64)
+    nq, d = Q.shape
+    n = K.shape[0]
+    sc = _scale(d, scale)
+    rows = np.asarray(rows, np.int64)
+    keys = np.asarray(keys, np.int64)
+    dq = np.zeros((rows.shape[0], d))
+    dk = np.zeros((keys.shape[0], d))
+    dvv = np.zeros((keys.shape[0], V.shape[1]))
+    for c0 in range(0, nq, chunk):
+        r = np.arange(c0, min(nq, c0 + chunk))
+        msk = dense_mask(n, causal, lts, lte, uts, ute, rows=r, n_rows=nq)
+        cols = np.nonzero(~msk.all(axis=0))[0]
+        if cols.size == 0:
+            continue                      # every row of the chunk sees nothing
+        P, _ = softmax_probs(Q[r], K[cols], msk[:, cols], sc)
+        dP = dO[r] @ V[cols].T
+        D = (P * dP).sum(axis=1)
+        dS = P * (dP - D[:, None])
+        # the requested keys among this chunk's columns
+        at = np.searchsorted(cols, keys)
+        hit = (at < cols.size) & (cols[np.minimum(at, cols.size - 1)] == keys)
+        if hit.any():
+            dvv[hit] += P[:, at[hit]].T @ dO[r]
+            dk[hit] += sc * (dS[:, at[hit]].T @ Q[r])
+        # the requested rows within this chunk
+        inside = (rows >= c0) & (rows < c0 + r.shape[0])
+        if inside.any():
+            dq[inside] = sc * (dS[rows[inside] - c0] @ K[cols])
     return dq, dk, dvv

@@ -176,3 +176,34 @@ def test_full_c5_d128(family):
     vec = I.config_masks(5, family)
     dq, dk, dv = run_case(q, k, v, do, vec)
     compare(q, k, v, do, vec, dq, dk, dv, heads=[(0, 0), (0, H - 1)])
+
+
+def test_long_sequence_list_in_rounds():
+    """Nq = 65600 rows (1025 query blocks of 64): the 128 global keys see every
+    row, so their key block's visible-tile list exceeds the 1024-entry list and
+    the dK/dV pass walks it in two rounds (the only backward case that does).
+    Every other key is open to a 512-row band from its own row (wide enough
+    that the global keys' share of each row, and so their |dV| summed over
+    65600 rows, stays well inside the bf16 bound). Checked on
+    sampled rows and keys of one head, against the oracle's sampled backward
+    (all rows evaluated: every row adds to the global keys' dK and dV)."""
+    B, H, N, d = 1, 8, 65600, 128
+    say(f"bwd long list-in-rounds B={B} H={H} N={N} d={d}")
+    j = np.arange(N)
+    glob = j < 128
+    lts = np.where(glob, N, j + 512).astype(np.int32)[None, None]  # masked below the band
+    lte = np.full((1, 1, N), N, np.int32)
+    uts = np.zeros((1, 1, N), np.int32)
+    ute = np.where(glob, 0, j).astype(np.int32)[None, None]        # masked above it
+    vec = (lts, lte, uts, ute, False)
+    q, k, v, do = (I.randn((B, H, N, d), 70_000 + t) for t in range(4))
+    dq, dk, dv = run_case(q, k, v, do, vec)
+    h = 5
+    rows = [0, 1, 127, 128, 20_000, 65_599]
+    keys = [0, 1, 63, 64, 127, 128, 1000, 40_000, 65_599]
+    rq, rk, rv = oracle.backward_sampled(q[0, h], k[0, h], v[0, h], do[0, h], False,
+                                         lts[0, 0], lte[0, 0], uts[0, 0], ute[0, 0],
+                                         rows=rows, keys=keys)
+    check_bf16("dQ", to_np(dq)[0, h, rows], rq)
+    check_bf16("dK", to_np(dk)[0, h, keys], rk)
+    check_bf16("dV", to_np(dv)[0, h, keys], rv)

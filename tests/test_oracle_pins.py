@@ -257,6 +257,25 @@ def test_backward_vs_sdpa_autograd(family):
     np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-11)
 
 
+@pytest.mark.parametrize("family", ["document", "sliding_window", "share_question", "causal"])
+def test_backward_sampled_vs_sdpa_autograd(family):
+    # chunks of 32 rows over 96 (so columns masked in a whole chunk are
+    # dropped from some chunks' softmax, and kept in others)
+    n, d = 96, 16
+    m = I.make_mask(family, n, np.random.default_rng(6))
+    allowed = torch.from_numpy(~oracle.dense_mask(n, m.causal, **_rows(m)))
+    q, k, v, do = (_rand((n, d), 180 + t) for t in range(4))
+    rows, keys = [0, 5, 31, 32, 70, 95], [0, 1, 40, 63, 64, 95]
+    dq, dk, dv = oracle.backward_sampled(q, k, v, do, m.causal, **_rows(m), rows=rows, keys=keys,
+                                         chunk=32)
+    tq, tk, tv = (torch.from_numpy(x.copy())[None, None].requires_grad_() for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=allowed[None, None])
+    (to * torch.from_numpy(do)[None, None]).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad[0, 0].numpy()[rows], atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad[0, 0].numpy()[keys], atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad[0, 0].numpy()[keys], atol=1e-11)
+
+
 # ------------------------------------------------------------- P7, P8 invariants
 
 def test_invariants():
