@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         const uint32_t mw = (key_row_mask(j, rb, Nk, causal, has_lt, has_ut, k_lts, k_lte, k_uts, k_ute) |
                              row_bits(Nq, rb + 32, rb)) >> (4 * hh);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[ib][r] = ((mw >> (8 * (r / 4) + r % 4)) & 1u) ? kNegInf : 0.f;
+        for (int r = 0; r < 16; ++r) sacc[ib][r] = mask_bias(mw, 8 * (r / 4) + r % 4);
       }
     } else {
 #pragma unroll

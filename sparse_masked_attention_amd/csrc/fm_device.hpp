@@ -69,6 +69,13 @@ __device__ inline int opaque_v(int x) {
   return x;
 }
 
+// The additive mask bias of one score: -inf where bit `bit` of w is set,
+// else 0, in two instructions (a signed one-bit field is 0 or all ones, and
+// all ones shifted left by 23 are the bits of -inf).
+__device__ inline float mask_bias(uint32_t w, uint32_t bit) {
+  return __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_sbfe((int)w, bit, 1u) << 23);
+}
+
 __device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

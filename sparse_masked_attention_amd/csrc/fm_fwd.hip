@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
           const int kl = kb32 * 32 + 8 * g + 4 * hh;
           const u32x4 w4 = *(const FM_LDS u32x4*)(FM_LDS uint32_t*)&mwords[w][kl];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sx[4 * g + e] = ((w4[e] >> l32) & 1u) ? kNegInf : 0.f;
+          for (int e = 0; e < 4; ++e) sx[4 * g + e] = mask_bias(w4[e], l32);
         }
       } else {
         sx = f32x16{};
