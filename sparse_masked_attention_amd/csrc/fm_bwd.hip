@@ -193,9 +193,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   // take items from work queues: queue qi holds the items t = n * nqueue + qi
   // in the order n = 0, 1, ..., which with 8 queues keeps every item of a
   // head on one XCD (workgroup g serves queue g % 8 and the hardware deals
-  // workgroups to the 8 XCDs in turn), heavy (early) key blocks first. Each
-  // workgroup takes its next item at the start of the current one, and ends
-  // when its queue is empty: every wave reaches the end.
+  // workgroups to the 8 XCDs in turn), heavy (early) key blocks first. A
+  // workgroup takes its next item once the current one's tiles are done, and
+  // ends when its queue is empty: every wave reaches the end.
   const int qi = kPersist ? (int)blockIdx.x % p.nqueue : 0;
   int item;
   if constexpr (kPersist) {
@@ -667,9 +667,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       store_rows(rdv, DV, std::integral_constant<int, C::DVO>{});
       __builtin_amdgcn_sched_barrier(0);
       // the next item's first two tiles, K, V and key bounds have landed;
-      // only the stores may be in flight. (Waited
-      // for on both paths, so that the compiler also sees K and V landed
-      // wherever the loop continues.)
+      // only the stores may be in flight. (Waited for on both paths, so that
+      // the compiler also sees K and V landed wherever the loop continues.)
       wait_vmcnt<C::NSTORE>();
       if (!more) break;
       zero_acc();
