@@ -34,7 +34,8 @@
  *   - Arguments are checked on the host before anything is enqueued. A failed
  *     check returns a status code and touches no output. A failed launch
  *     returns FM_ERROR_HIP. No exception crosses this interface and the
- *     library keeps no mutable global state.
+ *     library keeps no mutable global state beyond a per-device cache of
+ *     the compute-unit count (read once from the runtime).
  *   - B * H * N == 0 is a successful no-op. Offsets are 64-bit.
  *   - softmax_scale <= 0 or NaN selects 1/sqrt(d).
  *   - Supported (forward and backward): dtype FM_BF16 with d == dv in
