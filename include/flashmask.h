@@ -35,7 +35,8 @@
  *     check returns a status code and touches no output. A failed launch
  *     returns FM_ERROR_HIP. No exception crosses this interface and the
  *     library keeps no mutable global state beyond a per-device cache of
- *     the compute-unit count (read once from the runtime).
+ *     the compute-unit count (read from the runtime; safe to call from
+ *     several host threads at once).
  *   - B * H * N == 0 is a successful no-op. Offsets are 64-bit.
  *   - softmax_scale <= 0 or NaN selects 1/sqrt(d).
  *   - Supported (forward and backward): dtype FM_BF16 with d == dv in
@@ -136,9 +137,11 @@ fm_status_t flashmask_fwd(const void* q, const void* k, const void* v,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Backward. Given o and lse from flashmask_fwd with the same inputs and
- * dout [B,H,N,dv], writes dq, dk [B,H,N,d] and dv_out [B,H,N,dv] in dtype:
- * the analytic gradient of O = softmax(scale Q K^T + M) V,
+ * Backward (FlashMask README "Overview": the library ships forward and
+ * backward kernels; the gradient is the analytic one of the README
+ * "Formulation" expression). Given o and lse from flashmask_fwd with the
+ * same inputs and dout [B,H,N,dv], writes dq, dk [B,H,N,d] and dv_out
+ * [B,H,N,dv] in dtype: the analytic gradient of O = softmax(scale Q K^T + M) V,
  *   dV = P^T dO, dS = P * (dO V^T - rowsum(dO * O)), dQ = scale dS K,
  *   dK = scale dS^T Q.
  * tile_counts as in the forward, for flashmask_tile_shape(1, ...). All

@@ -33,6 +33,7 @@
 //     work queues) where the output rows can be staged through LDS: the next
 //     key block's scan, first tiles, K and V are under way before the
 //     finished block's dK and dV are stored.
+#include <atomic>
 #include <type_traits>
 
 #include "fm_device.hpp"
@@ -843,18 +844,20 @@ static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// compute units of the current device (cached per device)
+// compute units of the current device, cached per device. Host threads may
+// call this at once: each slot is an atomic, and a thread that finds it
+// empty queries the runtime and stores the (same) answer.
 static int cu_count() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int D, int DV>
