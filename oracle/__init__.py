@@ -12,8 +12,10 @@ force, closed forms, hand-worked fixtures).
 from .attention import (dense_mask, mask_row, forward, forward_rows, backward, backward_sampled,
                         softmax_probs)
 from .tables import kblock_minmax, classify, classify_counts, nnz_dense
+from .localize import rank_rows, local_bound, localize
+from . import bf16_replay
 from . import families
 
 __all__ = ["dense_mask", "mask_row", "forward", "forward_rows", "backward",
            "backward_sampled", "softmax_probs", "kblock_minmax", "classify", "classify_counts",
-           "nnz_dense", "families"]
+           "nnz_dense", "rank_rows", "local_bound", "localize", "bf16_replay", "families"]

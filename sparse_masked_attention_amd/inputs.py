@@ -34,7 +34,8 @@ __all__ = [
     "share_question_lengths", "share_question_from", "sliding_window",
     "block_sparse", "block_sparse_keep", "block_sparse_from",
     "doc_lengths_three", "doc_lengths_loguniform", "random_composition",
-    "stack_masks", "CONFIGS", "make_mask", "config_masks",
+    "stack_masks", "CONFIGS", "make_mask", "config_masks", "zigzag_chunks",
+    "chunk_rows",
 ]
 
 
@@ -369,3 +370,20 @@ def config_masks(config: int, family: str, s: int = 0, n: Optional[int] = None,
     ms = [make_mask(family, n, np.random.default_rng(mask_seed(config, s, b)))
           for b in range(B)]
     return stack_masks(ms)
+
+
+# ---------------------------------------------------------------- rank shares
+
+def zigzag_chunks(n: int, ranks: int, r: int):
+    """Query-row chunks of rank r of ``ranks`` in a zig-zag context-parallel
+    split (a common way to balance causal work over ranks): the rows are cut
+    into 2 * ranks equal pieces and rank r holds pieces r and 2 ranks - 1 - r,
+    as sorted (q0, q1) pairs."""
+    e = np.linspace(0, n, 2 * ranks + 1).astype(int)
+    return sorted([(int(e[r]), int(e[r + 1])), (int(e[2 * ranks - 1 - r]), int(e[2 * ranks - r]))])
+
+
+def chunk_rows(chunks) -> np.ndarray:
+    """Global row of every row a rank holds: its chunks' rows in order (used to
+    pick that rank's Q and dO rows)."""
+    return np.concatenate([np.arange(int(a), int(b)) for a, b in chunks]).astype(np.int64)

@@ -184,56 +184,3 @@ def test_repeatable_and_precomputed_table_and_canary():
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
     assert torch.equal(o1, o4) and torch.equal(l1, l4)
     assert torch.all(big_o[B * H * N * d:] == 7.0) and torch.all(big_l[B * H * N:] == 7.0)
-
-
-# ------------------------------------------------------------- full-size workloads
-def _sampled_rows_check(vec, q, k, v, o, lse, pairs, rows):
-    lts, lte, uts, ute, causal = vec
-    for b, h in pairs:
-        ro, rl = oracle.forward_rows(q[b, h], k[b, h], v[b, h], q.shape[2], causal,
-                                     oracle.mask_row(lts, b, h), oracle.mask_row(lte, b, h),
-                                     oracle.mask_row(uts, b, h), oracle.mask_row(ute, b, h),
-                                     rows=rows)
-        check_bf16(f"O[b{b},h{h}] sampled", to_np(o[b, h])[rows], ro)
-        check_lse(to_np(lse[b, h])[rows], rl, BF16_ATOL)
-
-
-def _sample_rows(N, rng, count=384):
-    edge = np.array([0, 1, N - 2, N - 1])
-    return np.unique(np.concatenate([edge, rng.choice(N, count, replace=False)]))
-
-
-@pytest.mark.parametrize("family", ["document", "causal", "all_open"])
-def test_full_c2(family):
-    c = I.CONFIGS[2]
-    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
-    say(f"fwd full C2 family={family}")
-    q, k, v = (I.randn((B, H, N, d), I.qkv_seed(2, t)) for t in range(3))
-    vec = I.config_masks(2, family)
-    o, lse = run_fwd(q, k, v, vec, torch.bfloat16)
-    rng = np.random.default_rng(0)
-    _sampled_rows_check(vec, q, k, v, o, lse, [(0, 0), (0, H - 1)], _sample_rows(N, rng))
-
-
-@pytest.mark.parametrize("family", ["share_question", "sliding_window"])
-def test_full_c3(family):
-    c = I.CONFIGS[3]
-    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
-    say(f"fwd full C3 family={family}")
-    q, k, v = (I.randn((B, H, N, d), I.qkv_seed(3, t)) for t in range(3))
-    vec = I.config_masks(3, family)
-    o, lse = run_fwd(q, k, v, vec, torch.bfloat16)
-    rng = np.random.default_rng(1)
-    _sampled_rows_check(vec, q, k, v, o, lse, [(0, 5), (1, 30)], _sample_rows(N, rng, 256))
-
-
-@pytest.mark.parametrize("family", ["prefix_lm_document", "block_sparse"])
-def test_full_c4(family):
-    c = I.CONFIGS[4]
-    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
-    say(f"fwd full C4 family={family}")
-    q, k, v = (I.randn((B, H, N, d), I.qkv_seed(4, t)) for t in range(3))
-    vec = I.config_masks(4, family)
-    o, lse = run_fwd(q, k, v, vec, torch.bfloat16)
-    rng = np.random.default_rng(2)
-    _sampled_rows_check(vec, q, k, v, o, lse, [(0, 3)], _sample_rows(N, rng, 256))

@@ -12,7 +12,7 @@ import torch
 import oracle
 from sparse_masked_attention_amd import inputs as I
 from sparse_masked_attention_amd import _binding as fm
-from gpu_util import BF16_ATOL, check_bf16, check_lse, mask_from, say, to_dev, to_np
+from gpu_util import BF16_ATOL, check_bf16, check_lse, mask_from, replays, say, to_dev, to_np
 from _lib_fixture import ensure_built
 
 pytestmark = pytest.mark.gpu
@@ -49,11 +49,12 @@ def compare(q, k, v, do, vec, got, heads=None):
     sel = (lambda x: x) if heads is None else (lambda x: np.stack([x[b, h] for b, h in heads]))
     o, lse, dq, dk, dv = (to_np(x) for x in got)
     assert o.shape[-1] == DV and dq.shape[-1] == D and dk.shape[-1] == D and dv.shape[-1] == DV
-    check_bf16("O", sel(o), sel(ro))
+    rf, rb = replays(q, k, v, do, vec, heads=heads)
+    check_bf16("O", sel(o), sel(ro), replay=rf[0])
     check_lse(sel(lse), sel(rl), BF16_ATOL)
-    check_bf16("dQ", sel(dq), sel(rq))
-    check_bf16("dK", sel(dk), sel(rk))
-    check_bf16("dV", sel(dv), sel(rv))
+    check_bf16("dQ", sel(dq), sel(rq), replay=rb[0])
+    check_bf16("dK", sel(dk), sel(rk), replay=rb[1])
+    check_bf16("dV", sel(dv), sel(rv), replay=rb[2])
 
 
 FAMILIES = ["causal", "document", "share_question", "sliding_window", "block_sparse",

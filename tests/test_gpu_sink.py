@@ -7,9 +7,9 @@ import torch
 
 import oracle
 from sparse_masked_attention_amd import inputs as I
-from sparse_masked_attention_amd import localize as L
 from sparse_masked_attention_amd import _binding as fm
-from gpu_util import BF16_ATOL, FP32_ATOL, check_bf16, check_fp32, check_lse, mask_from, say, to_dev, to_np
+from gpu_util import (BF16_ATOL, FP32_ATOL, check_bf16, check_fp32, check_lse, mask_from, replays, say,
+                      to_dev, to_np)
 from _lib_fixture import ensure_built
 
 pytestmark = pytest.mark.gpu
@@ -34,12 +34,15 @@ def compare(q, k, v, do, vec, sink, got, fp32=False):
     ro, rl = oracle.forward(q, k, v, causal, lts, lte, uts, ute, sink=sink)
     rq, rk, rv, rs = oracle.backward(q, k, v, do, causal, lts, lte, uts, ute, sink=sink)
     o, lse, dq, dk, dv, ds = (to_np(x) for x in got)
-    check = check_fp32 if fp32 else check_bf16
-    check("O", o, ro)
     check_lse(lse, rl, FP32_ATOL if fp32 else BF16_ATOL)
-    check("dQ", dq, rq)
-    check("dK", dk, rk)
-    check("dV", dv, rv)
+    if fp32:
+        for name, g, r in (("O", o, ro), ("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            check_fp32(name, g, r)
+    else:
+        rf, rb = replays(q, k, v, do, vec, sink=np.asarray(sink, np.float32))
+        check_bf16("O", o, ro, replay=rf[0])
+        for i, (name, g, r) in enumerate((("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv))):
+            check_bf16(name, g, r, replay=rb[i])
     err = np.abs(ds - rs)
     say(f"  dsink: max_abs={err.max():.3e} ref={np.round(rs, 3)}")
     tol = (1e-4 if fp32 else 2e-2) + (1e-5 if fp32 else 5e-3) * np.abs(rs)
@@ -95,13 +98,14 @@ def test_sink_on_a_rank_share_and_deterministic():
     vec = I.stack_masks([I.make_mask("document", n, np.random.default_rng(11))])
     e = np.linspace(0, n, 9).astype(int)
     chunks = [(int(e[2]), int(e[3])), (int(e[5]), int(e[6]))]
-    rows = L.local_rows(chunks, n)
-    l4 = L.localize(*vec[:4], vec[4], chunks, n)
+    rows = oracle.rank_rows(chunks, n)
+    l4 = oracle.localize(*vec[:4], vec[4], chunks, n)      # the oracle's side
     q, k, v, do = (I.randn((B, H, n, d), 4300 + t) for t in range(4))
     sink = np.array([0.3, 2.0])
     lvec = (l4[0], l4[1], l4[2], l4[3], False)
-    g1 = run(q[:, :, rows], k, v, do[:, :, rows], mask_from(lvec), sink)
+    lm = fm.localize(mask_from(vec), B, n, n, chunks)      # the GPU's side
+    g1 = run(q[:, :, rows], k, v, do[:, :, rows], lm, sink)
     compare(q[:, :, rows], k, v, do[:, :, rows], lvec, sink, g1)
-    g2 = run(q[:, :, rows], k, v, do[:, :, rows], mask_from(lvec), sink)
+    g2 = run(q[:, :, rows], k, v, do[:, :, rows], lm, sink)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)

@@ -14,7 +14,6 @@ import torch
 
 import oracle
 from sparse_masked_attention_amd import inputs as I
-from sparse_masked_attention_amd import localize as L
 
 pytestmark = pytest.mark.filterwarnings("ignore")
 
@@ -57,10 +56,45 @@ def test_local_mask_is_the_rows_it_holds(family, seed):
     glob = oracle.dense_mask(n, causal, lts, lte, uts, ute)
     for part in _chunkings(rng, n):
         for ch in part:
-            l4 = L.localize(*vec[:4], causal, ch, n)
-            rows = L.local_rows(ch, n)
+            l4 = oracle.localize(*vec[:4], causal, ch, n)
+            rows = oracle.rank_rows(ch, n)
             loc = oracle.dense_mask(n, False, *[x[0, 0] for x in l4[:4]], n_rows=len(rows))
             np.testing.assert_array_equal(loc, glob[rows])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_local_bound_counts_the_rows_before(seed):
+    """local(t) is the number of the rank's rows that lie before global row t
+    (brute force over every t, also outside [0, n])."""
+    rng = np.random.default_rng(400 + seed)
+    n = int(rng.integers(2, 90))
+    for part in _chunkings(rng, n):
+        for ch in part:
+            rows = oracle.rank_rows(ch, n)
+            for t in range(-4, n + 5):
+                assert oracle.local_bound(t, ch) == int((rows < t).sum())
+
+
+def test_localize_matches_numpy_clip_form():
+    """The plain loops of oracle.localize against the closed clip form written
+    with numpy broadcasting (same reading, independent code)."""
+    rng = np.random.default_rng(9)
+    n = 200
+    v = [rng.integers(-300, 300, (2, 1, n)).astype(np.int32) for _ in range(4)]
+    ch = [(5, 40), (90, 91), (120, 200)]
+    a = np.array([c[0] for c in ch])[:, None, None, None]
+    ln = np.array([c[1] - c[0] for c in ch])[:, None, None, None]
+    clip = lambda t: np.clip(t[None].astype(np.int64) - a, 0, ln).sum(axis=0)
+    for causal in (True, False):
+        got = oracle.localize(*v, causal, ch, n)
+        np.testing.assert_array_equal(got[0], clip(v[0]))
+        np.testing.assert_array_equal(got[1], clip(v[1]))
+        if causal:
+            np.testing.assert_array_equal(got[2], 0)
+            np.testing.assert_array_equal(got[3], clip(np.broadcast_to(np.arange(n), v[0].shape)))
+        else:
+            np.testing.assert_array_equal(got[2], clip(v[2]))
+            np.testing.assert_array_equal(got[3], clip(v[3]))
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -72,8 +106,8 @@ def test_localisation_on_arbitrary_int32_bounds(seed):
         glob = oracle.dense_mask(n, causal, *v)
         for part in _chunkings(rng, n):
             for ch in part:
-                l4 = L.localize(*[x[None, None] for x in v], causal, ch, n)
-                rows = L.local_rows(ch, n)
+                l4 = oracle.localize(*[x[None, None] for x in v], causal, ch, n)
+                rows = oracle.rank_rows(ch, n)
                 loc = oracle.dense_mask(n, False, *[x[0, 0] for x in l4[:4]], n_rows=len(rows))
                 np.testing.assert_array_equal(loc, glob[rows])
 
@@ -90,8 +124,8 @@ def test_rank_forward_and_backward_recompose_the_global_ones(family):
     for part in _chunkings(rng, n):
         sk, sv = np.zeros_like(gk), np.zeros_like(gv)
         for ch in part:
-            rows = L.local_rows(ch, n)
-            l4 = L.localize(lts, lte, uts, ute, causal, ch, n)
+            rows = oracle.rank_rows(ch, n)
+            l4 = oracle.localize(lts, lte, uts, ute, causal, ch, n)
             lo, ll = oracle.forward(q[:, :, rows], k, v, False, *l4[:4])
             np.testing.assert_allclose(lo, go[:, :, rows], atol=1e-12)
             np.testing.assert_array_equal(np.isneginf(ll), np.isneginf(gl[:, :, rows]))
