@@ -212,6 +212,35 @@ fm_status_t flashmask_bwd_qk(const void* q, const void* k, const void* v,
                              int64_t* tile_counts,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward that allocates nothing and takes no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). Same arguments and
+ * results as flashmask_bwd_qk without `workspace` / `workspace_bytes`: the
+ * workspace is a static device array of FLASHMASK_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per GPU, held until the process ends (its address
+ * is looked up once per device on the first call). A problem whose
+ * flashmask_workspace_size_qk(1, ...) exceeds that returns
+ * FM_ERROR_WORKSPACE_TOO_SMALL before anything is enqueued (16 MiB holds
+ * B * H * Nq up to about 1.3 million query rows). The array keeps the last
+ * call's contents; every call writes what it reads before reading it (the
+ * work-queue counters are reset by the call's own first kernel, no memset).
+ * All calls on one GPU share the array: calls that may overlap on one GPU
+ * (on different streams, or from several host threads) race and must be
+ * serialised by the caller.
+ */
+#define FLASHMASK_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+fm_status_t flashmask_bwd_noalloc(const void* q, const void* k, const void* v,
+                                  const void* o, const float* lse, const void* dout,
+                                  const int32_t* lts, const int32_t* lte,
+                                  const int32_t* uts, const int32_t* ute, int hm,
+                                  const int32_t* kblock_minmax,
+                                  int B, int H, int Nq, int Nk, int d, int dv, fm_dtype_t dtype,
+                                  int causal, float softmax_scale, const float* sink,
+                                  void* dq, void* dk, void* dv_out, float* dsink,
+                                  int64_t* tile_counts, void* stream);
+
 /* Largest nchunks flashmask_localize accepts. */
 int flashmask_max_chunks(void);
 

@@ -49,6 +49,9 @@ _SIGNATURES = {
     "flashmask_bwd_qk": (_c_int, [_c_void_p] * 6 + [_c_void_p] * 4 + [_c_int, _c_void_p]
                          + [_c_int] * 6 + [_c_int, _c_int, _c_float, _c_void_p]
                          + [_c_void_p] * 5 + [_c_void_p, _c_size_t, _c_void_p]),
+    "flashmask_bwd_noalloc": (_c_int, [_c_void_p] * 6 + [_c_void_p] * 4 + [_c_int, _c_void_p]
+                              + [_c_int] * 6 + [_c_int, _c_int, _c_float, _c_void_p]
+                              + [_c_void_p] * 5 + [_c_void_p]),
     "flashmask_max_chunks": (_c_int, []),
     "flashmask_localize": (_c_int, [_c_void_p] * 4 + [_c_int] * 5 + [_c_void_p, _c_int]
                            + [_c_void_p] * 4 + [_c_void_p]),

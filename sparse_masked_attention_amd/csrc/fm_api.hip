@@ -1,10 +1,19 @@
 // C ABI: argument checks, workspace layout and dispatch. Declarations and the
 // contract of every entry point are in include/flashmask.h.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
 #include "../../include/flashmask.h"
 #include "fm_internal.hpp"
+
+namespace fm {
+// The workspace of flashmask_bwd_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends. In host code `scratch` names a host
+// stand-in, never the device memory: its device address comes from
+// hipGetSymbolAddress, once per device (scratch_address below).
+__device__ __align__(256) char scratch[FLASHMASK_NOALLOC_SCRATCH_BYTES];
+}  // namespace fm
 
 namespace {
 
@@ -70,6 +79,21 @@ fm::MaskArgs mask_args(const int32_t* lts, const int32_t* lte, const int32_t* ut
 float resolve_scale(float s, int d) {
   if (!(s > 0.f)) return 1.0f / std::sqrt((float)d);  // also catches NaN
   return s;
+}
+
+// Device address of this GPU's `scratch`, looked up on the first call made
+// with that device current and kept per device (atomic slots: host threads
+// may race here, and each stores the same address). nullptr on a HIP error.
+void* scratch_address() {
+  static std::atomic<void*> slots[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = slots[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(fm::scratch)) != hipSuccess || p == nullptr) return nullptr;
+    slots[dev].store(p, std::memory_order_release);
+  }
+  return p;
 }
 
 }  // namespace
@@ -284,6 +308,28 @@ fm_status_t flashmask_bwd(const void* q, const void* k, const void* v, const voi
   return flashmask_bwd_qk(q, k, v, o, lse, dout, lts, lte, uts, ute, hm, kblock_minmax, B, H, N, N,
                           d, dv, dtype, causal, softmax_scale, nullptr, dq, dk, dv_out, nullptr,
                           tile_counts, workspace, workspace_bytes, stream);
+}
+
+fm_status_t flashmask_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout, const int32_t* lts,
+                                  const int32_t* lte, const int32_t* uts, const int32_t* ute, int hm,
+                                  const int32_t* kblock_minmax, int B, int H, int Nq, int Nk, int d,
+                                  int dv, fm_dtype_t dtype, int causal, float softmax_scale,
+                                  const float* sink, void* dq, void* dk, void* dv_out, float* dsink,
+                                  int64_t* tile_counts, void* stream) {
+  fm_status_t st = check_common(B, H, Nq, Nk, d, dv, dtype, hm, uts, ute, causal);
+  if (st != FM_SUCCESS) return st;
+  const size_t need = flashmask_workspace_size_qk(1, B, H, Nq, Nk, d, dv, hm, dtype);
+  if (need > (size_t)FLASHMASK_NOALLOC_SCRATCH_BYTES) return FM_ERROR_WORKSPACE_TOO_SMALL;
+  if ((long long)B * H * (Nq > Nk ? Nq : Nk) == 0)   // no row or key: needs no workspace
+    return flashmask_bwd_qk(q, k, v, o, lse, dout, lts, lte, uts, ute, hm, kblock_minmax, B, H, Nq,
+                            Nk, d, dv, dtype, causal, softmax_scale, sink, dq, dk, dv_out, dsink,
+                            tile_counts, nullptr, 0, stream);
+  void* ws = scratch_address();
+  if (ws == nullptr) return FM_ERROR_HIP;
+  return flashmask_bwd_qk(q, k, v, o, lse, dout, lts, lte, uts, ute, hm, kblock_minmax, B, H, Nq, Nk,
+                          d, dv, dtype, causal, softmax_scale, sink, dq, dk, dv_out, dsink, tile_counts,
+                          ws, (size_t)FLASHMASK_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int flashmask_max_chunks(void) { return fm::kMaxChunks; }

@@ -32,7 +32,7 @@ def test_header_declares_the_abi():
               "flashmask_workspace_size", "flashmask_status_string", "flashmask_table_block",
               "flashmask_tile_shape", "flashmask_tile_classify_qk", "flashmask_fwd_qk",
               "flashmask_bwd_qk", "flashmask_workspace_size_qk", "flashmask_localize",
-              "flashmask_max_chunks"]:
+              "flashmask_max_chunks", "flashmask_bwd_noalloc"]:
         assert n in names
 
 
@@ -186,3 +186,23 @@ def test_localize_argument_checks(lib):
     assert call(list(range(0, 2 * 65 * 1, 1)), n_rows=1000) == FM_INVALID  # too many chunks
     assert call([0, 10], Nk=0) == FM_SUCCESS            # no key column: nothing to write
     assert call([0, 10], outs=None) == FM_INVALID
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    """flashmask_bwd_noalloc refuses a problem whose workspace exceeds its
+    static scratch (16 MiB) on the host, before anything is enqueued; bad
+    arguments are refused as in the other entry points."""
+    p = lambda v: ctypes.c_void_p(v)
+    scratch = 16 << 20
+
+    def call(B, H, Nq, Nk, d=128, dv=128, hm=1, dtype=1):
+        return lib.flashmask_bwd_noalloc(p(16), p(16), p(16), p(16), p(16), p(16), p(16), None,
+                                         None, None, hm, None, B, H, Nq, Nk, d, dv, dtype, 1,
+                                         ctypes.c_float(0.0), None, p(16), p(16), p(16), None, None,
+                                         None)
+    # 3 float32 row arrays of B*H*Nq plus the table: 32 heads x 65536 rows is 24 MiB
+    assert _binding.lib().flashmask_workspace_size_qk(1, 1, 32, 65536, 65536, 128, 128, 1, 1) > scratch
+    assert call(1, 32, 65536, 65536) == FM_WS_SMALL
+    assert call(1, 1, 100, 100, hm=2) == FM_INVALID          # hm not in {1, H}
+    assert call(1, 1, 100, 100, d=96, dv=96) == FM_NOT_SUPPORTED
+    assert call(0, 4, 100, 100) == FM_SUCCESS                 # empty problem: a no-op
