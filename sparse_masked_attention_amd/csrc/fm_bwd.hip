@@ -203,7 +203,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     if (tid == 0) next_item = atomicAdd(p.queue + qi, 1);
     __syncthreads();
     item = uniform(next_item);         // the same value in every lane and wave
-    if (item >= p.per_queue) return;
+    // unsigned: a counter holding anything but a ticket of this call ends
+    // the workgroup instead of naming an item
+    if ((unsigned)item >= (unsigned)p.per_queue) return;
   } else {
     item = (int)blockIdx.x;
   }
@@ -624,7 +626,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       if (tid == 0) next_item = atomicAdd(p.queue + qi, 1);
       __syncthreads();
       const int nitem = uniform(next_item);
-      const bool more = nitem < p.per_queue;   // the same in every wave
+      const bool more = (unsigned)nitem < (unsigned)p.per_queue;   // the same in every wave
       if (more) {
         // Start the next item before this one's stores: its scan, its first
         // two tiles (stages 0 and 1), then its K, V and key bounds. The
