@@ -40,9 +40,9 @@
  *   - B * H * N == 0 is a successful no-op. Offsets are 64-bit.
  *   - softmax_scale <= 0 or NaN selects 1/sqrt(d).
  *   - Supported (forward and backward): dtype FM_BF16 with d == dv in
- *     {64, 128, 256} or d = 192 with dv = 128 (Q/K head dim larger than V's,
- *     README "News": large head dims); FM_FP32 with d == dv in {64, 128}.
- *     Others: FM_ERROR_NOT_SUPPORTED.
+ *     {64, 128, 256, 512} or d = 192 with dv = 128 (Q/K head dim larger than
+ *     V's; README "News" and "Key Features": large head dims); FM_FP32 with
+ *     d == dv in {64, 128, 256}. Others: FM_ERROR_NOT_SUPPORTED.
  */
 #ifndef FLASHMASK_H
 #define FLASHMASK_H

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "lib", "libflashmask.so")
-SOURCES = ["fm_api.hip", "fm_classify.hip", "fm_fwd.hip", "fm_bwd.hip", "fm_localize.hip"]
+SOURCES = ["fm_api.hip", "fm_classify.hip", "fm_fwd.hip", "fm_bwd.hip", "fm_localize.hip",
+           "fm_wide.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -117,7 +117,7 @@ fm_status_t flashmask_tile_shape(int is_bwd, int d, fm_dtype_t dtype, int* block
   if (block_q == nullptr || block_k == nullptr) return FM_ERROR_INVALID_VALUE;
   if (!supported_d(d, dtype)) return FM_ERROR_NOT_SUPPORTED;
   *block_q = is_bwd ? fm::bwd_block_q(d, dtype == FM_BF16) : fm::fwd_block_q(d, dtype == FM_BF16);
-  *block_k = is_bwd ? fm::kBwdBlockK : fm::kFwdBlockK;
+  *block_k = is_bwd ? fm::bwd_block_k(d, dtype == FM_BF16) : fm::kFwdBlockK;
   return FM_SUCCESS;
 }
 

@@ -68,10 +68,10 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------- preprocess
-// fp32 path: delta_i = sum_m dO[i][m] * O[i][m] in float32; LSE in base-2
-// units (+inf where the row is fully masked, so exp2(s - LSE2) is 0 there).
-// 16 threads per row, 16-byte chunks. (The bf16 path computes delta and the
-// base-2 LSE inside its dQ pass.)
+// fp32 path and the wide head dims: delta_i = sum_m dO[i][m] * O[i][m] in
+// float32; LSE in base-2 units (+inf where the row is fully masked, so
+// exp2(s - LSE2) is 0 there). 16 threads per row, 16-byte chunks. (The
+// other bf16 dims compute delta and the base-2 LSE inside their dQ pass.)
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   const long long rows = (long long)p.B * p.H * p.Nq;
@@ -1027,6 +1027,13 @@ static hipError_t launch_bwd_main(const AttnArgs& a, hipStream_t stream) {
   p.sl2 = a.scale * kLog2e;
   p.nkb = (a.Nk + kBwdBlockK - 1) / kBwdBlockK;
   p.nkb64 = (a.Nk + kTableBlock - 1) / kTableBlock;
+  if (wide_dims(a.d, a.dv, a.is_bf16)) {
+    // delta and the base-2 LSE, then the wide dQ and dK/dV passes
+    p.nqb = (p.Nq + 31) / 32;
+    const hipError_t e = a.is_bf16 ? launch_pre<512, bf16>(p, stream) : launch_pre<256, float>(p, stream);
+    if (e != hipSuccess) return e;
+    return launch_wide_bwd(a, stream);
+  }
   if (a.is_bf16) {
     // the bf16 (d, dv) pairs compiled in (kept in step with bf16_dims())
     if (a.d == 64 && a.dv == 64) return launch_bwd_bf16<64, 64>(p, a, stream);

@@ -202,6 +202,32 @@ __device__ inline uint32_t key_row_mask(int j, int q0, int N, bool causal, bool 
   return j >= N ? ~0u : m;
 }
 
+// ---------------------------------------------------------------- row epilogue
+// From a row's sum lt of exp(S - m) over its open keys (m the running
+// offset, in raw score units before `scale`): the factor that turns the
+// accumulated sum of P V into O, and the natural-log LSE. With a sink logit
+// s (one more always-open entry with a zero value vector) the normaliser
+// becomes exp(lse0) + exp(s): LSE = logaddexp(lse0, s), computed in the log
+// domain so a large s cannot overflow, and O shrinks by exp(lse0 - LSE). A
+// row with nothing open has O = 0 and LSE = -inf (s with a sink).
+__device__ inline void finish_row(float lt, float m, float scale, float s, bool has_sink,
+                                  float& inv, float& lse) {
+  if (!(lt > 0.f)) {
+    inv = 0.f;
+    lse = has_sink ? s : kNegInf;
+    return;
+  }
+  const float lse0 = m * scale + __logf(lt);
+  if (!has_sink) {
+    inv = 1.f / lt;
+    lse = lse0;
+    return;
+  }
+  const float hi = fmaxf(lse0, s);
+  lse = hi + log1pf(__expf(-fabsf(lse0 - s)));
+  inv = __expf(lse0 - lse) / lt;
+}
+
 // ---------------------------------------------------------------- mask rule
 // Per key block: min/max of LTS, LTE, UTS, UTE (8 int32, in that order).
 struct BlockBounds {

@@ -85,32 +85,6 @@ __device__ inline void mask_block(f32x16& s, const FM_LDS int* vl, int kl0, int 
   }
 }
 
-// ---------------------------------------------------------------- row epilogue
-// From a row's sum lt of exp(S - m) over its open keys (m the running
-// offset, in raw score units before `scale`): the factor that turns the
-// accumulated sum of P V into O, and the natural-log LSE. With a sink logit
-// s (one more always-open entry with a zero value vector) the normaliser
-// becomes exp(lse0) + exp(s): LSE = logaddexp(lse0, s), computed in the log
-// domain so a large s cannot overflow, and O shrinks by exp(lse0 - LSE). A
-// row with nothing open has O = 0 and LSE = -inf (s with a sink).
-__device__ inline void finish_row(float lt, float m, float scale, float s, bool has_sink,
-                                  float& inv, float& lse) {
-  if (!(lt > 0.f)) {
-    inv = 0.f;
-    lse = has_sink ? s : kNegInf;
-    return;
-  }
-  const float lse0 = m * scale + __logf(lt);
-  if (!has_sink) {
-    inv = 1.f / lt;
-    lse = lse0;
-    return;
-  }
-  const float hi = fmaxf(lse0, s);
-  lse = hi + log1pf(__expf(-fabsf(lse0 - s)));
-  inv = __expf(lse0 - lse) / lt;
-}
-
 // ---------------------------------------------------------------- bf16 kernel
 // One query-major kernel serves two passes:
 //   MODE 0, forward: O and LSE with online softmax;
@@ -975,6 +949,7 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.sl2 = a.scale * kLog2e;
   p.nkb = (a.Nk + kFwdBlockK - 1) / kFwdBlockK;
+  if (wide_dims(a.d, a.dv, a.is_bf16)) return launch_wide_fwd(a, stream);
   if (a.is_bf16) {
     return dispatch_qmajor<kModeFwd>(a.d, a.dv, p, stream);
   } else {

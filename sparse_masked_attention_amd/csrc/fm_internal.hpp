@@ -17,12 +17,17 @@ inline int fwd_block_q(int d, int is_bf16) { (void)d; (void)is_bf16; return 128;
 constexpr int kBwdBlockK = 128;
 // backward query-block height: 64 rows for bf16 with d <= 128, else 32
 inline int bwd_block_q(int d, int is_bf16) { return (is_bf16 && d <= 128) ? 64 : 32; }
+inline bool wide_dims(int d, int dv, bool is_bf16);
+// backward key-block width: 64 keys at the wide head dims, else kBwdBlockK
+inline int bwd_block_k(int d, int is_bf16) { return wide_dims(d, d, is_bf16 != 0) ? 64 : kBwdBlockK; }
 
 // Head dims with kernels compiled in: (d, dv) pairs for bf16, d == dv for fp32.
 inline bool bf16_dims(int d, int dv) {
-  return (d == dv && (d == 64 || d == 128 || d == 256)) || (d == 192 && dv == 128);
+  return (d == dv && (d == 64 || d == 128 || d == 256 || d == 512)) || (d == 192 && dv == 128);
 }
-inline bool fp32_dims(int d, int dv) { return d == dv && (d == 64 || d == 128); }
+inline bool fp32_dims(int d, int dv) { return d == dv && (d == 64 || d == 128 || d == 256); }
+// the wide head dims (bf16 d = dv = 512, fp32 d = dv = 256), served by fm_wide.hip
+inline bool wide_dims(int d, int dv, bool is_bf16) { return d == dv && d == (is_bf16 ? 512 : 256); }
 
 struct MaskArgs {
   const int32_t* lts;  // [B, hm, Nk] or nullptr
@@ -73,5 +78,9 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_sink_zero(const float* sink, float* dsink, int H, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnArgs& a, hipStream_t stream);
+// wide head dims: the forward; the backward's dQ and dK/dV passes (delta and
+// the base-2 LSE already in the workspace)
+hipError_t launch_wide_fwd(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_wide_bwd(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace fm

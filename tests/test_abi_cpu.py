@@ -63,6 +63,11 @@ def test_table_block_and_tile_shapes(lib):
     # d = 192 exists for bf16 (with dv = 128) only
     assert _binding.tile_shape(False, 192, torch.bfloat16) == (128, 64)
     assert _binding.tile_shape(True, 192, torch.bfloat16) == (32, 128)
+    # the wide head dims: 64-key backward blocks
+    assert _binding.tile_shape(False, 512, torch.bfloat16) == (128, 64)
+    assert _binding.tile_shape(True, 512, torch.bfloat16) == (32, 64)
+    assert _binding.tile_shape(False, 256, torch.float32) == (128, 64)
+    assert _binding.tile_shape(True, 256, torch.float32) == (32, 64)
     with pytest.raises(_binding.FlashMaskError):
         _binding.tile_shape(False, 96, torch.bfloat16)
     with pytest.raises(_binding.FlashMaskError):
@@ -105,7 +110,9 @@ def test_fwd_argument_checks(lib):
     assert _fwd_call(lib, d=192, dv=192) == FM_NOT_SUPPORTED
     assert _fwd_call(lib, d=128, dv=192) == FM_NOT_SUPPORTED
     assert _fwd_call(lib, dtype=0, d=192, dv=128) == FM_NOT_SUPPORTED
-    assert _fwd_call(lib, dtype=0, d=256, dv=256) == FM_NOT_SUPPORTED
+    assert _fwd_call(lib, dtype=0, d=512, dv=512) == FM_NOT_SUPPORTED
+    assert _fwd_call(lib, d=512, dv=256) == FM_NOT_SUPPORTED
+    assert _fwd_call(lib, d=384, dv=384) == FM_NOT_SUPPORTED
     assert _fwd_call(lib, dtype=7) == FM_INVALID
     assert _fwd_call(lib, ws=None) == FM_WS_SMALL
     assert _fwd_call(lib, ws=1, ws_bytes=8) == FM_WS_SMALL

@@ -1,0 +1,159 @@
+"""Parity at the wide head dims: bf16 with d = dv = 512 and fp32 with
+d = dv = 256 (the README lists large head dims among FlashMask's features,
+"News" and "Key Features"; the scale stays 1/sqrt(d), "Formulation").
+
+Forward and backward against the fp64 oracle on every mask family at
+N in {129, 1000}, ragged small N, a sink, Nq != Nk, the tile counters at
+the reported tile shapes, bitwise repeatability, and a full-size
+B=1 H=4 N=8192 case with whole-head checks on two heads (bf16). bf16 values
+follow the replay-aware rule of gpu_util.check_bf16; fp32 the fixed 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_masked_attention_amd import inputs as I
+from sparse_masked_attention_amd import _binding as fm
+from gpu_util import (BF16_ATOL, FP32_ATOL, check_bf16, check_fp32, check_lse, mask_from, replays, say,
+                      to_dev, to_np)
+from _lib_fixture import ensure_built
+
+pytestmark = pytest.mark.gpu
+
+WIDE = [(512, torch.bfloat16), (256, torch.float32)]
+FAMILIES = ["causal", "document", "share_question", "sliding_window", "block_sparse",
+            "prefix_lm_document", "all_open"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_built()
+
+
+def _inputs(B, H, Nq, Nk, d, seed, bf):
+    q = I.randn((B, H, Nq, d), seed, bf16=bf)
+    k = I.randn((B, H, Nk, d), seed + 1, bf16=bf)
+    v = I.randn((B, H, Nk, d), seed + 2, bf16=bf)
+    do = I.randn((B, H, Nq, d), seed + 3, bf16=bf)
+    return q, k, v, do
+
+
+def _run(q, k, v, do, vec, dtype, sink=None, fcounts=None, bcounts=None):
+    m = mask_from(vec)
+    qd, kd, vd, dod = (to_dev(x, dtype) for x in (q, k, v, do))
+    s = None if sink is None else torch.from_numpy(np.asarray(sink, np.float32)).cuda()
+    o, lse = fm.fwd(qd, kd, vd, m, sink=s, tile_counts=fcounts)
+    g = fm.bwd(qd, kd, vd, o, lse, dod, m, sink=s, tile_counts=bcounts)
+    torch.cuda.synchronize()
+    return (o, lse) + tuple(g)
+
+
+def _compare(q, k, v, do, vec, got, dtype, sink=None, heads=None):
+    lts, lte, uts, ute, causal = vec
+    ro, rl = oracle.forward(q, k, v, causal, lts, lte, uts, ute, sink=sink, heads=heads)
+    rb_all = oracle.backward(q, k, v, do, causal, lts, lte, uts, ute, sink=sink, heads=heads)
+    sel = (lambda x: x) if heads is None else (lambda x: np.stack([x[b, h] for b, h in heads]))
+    o, lse, dq, dk, dv = (to_np(x) for x in got[:5])
+    if dtype == torch.float32:
+        check_lse(sel(lse), sel(rl), FP32_ATOL)
+        for name, g, r in zip(("O", "dQ", "dK", "dV"), (o, dq, dk, dv), (ro,) + tuple(rb_all[:3])):
+            check_fp32(name, sel(g), sel(r))
+    else:
+        rf, rb = replays(q, k, v, do, vec, heads=heads,
+                         sink=None if sink is None else np.asarray(sink, np.float32))
+        check_bf16("O", sel(o), sel(ro), replay=rf[0])
+        check_lse(sel(lse), sel(rl), BF16_ATOL)
+        for i, (name, g, r) in enumerate(zip(("dQ", "dK", "dV"), (dq, dk, dv), rb_all[:3])):
+            check_bf16(name, sel(g), sel(r), replay=rb[i])
+    if sink is not None:
+        ds, rs = to_np(got[5]), rb_all[3]
+        fp32 = dtype == torch.float32
+        tol = (1e-4 if fp32 else 2e-2) + (1e-5 if fp32 else 5e-3) * np.abs(rs)
+        say(f"  dsink: max_abs={np.abs(ds - rs).max():.3e}")
+        assert (np.abs(ds - rs) <= tol).all(), (ds, rs)
+
+
+@pytest.mark.parametrize("family", FAMILIES)
+@pytest.mark.parametrize("N", [129, 1000])
+@pytest.mark.parametrize("d,dtype", WIDE)
+def test_families(d, dtype, family, N):
+    bf = dtype == torch.bfloat16
+    say(f"wide d={d} {dtype} family={family} N={N}")
+    q, k, v, do = _inputs(1, 2, N, N, d, 8000, bf)
+    vec = I.stack_masks([I.make_mask(family, N, np.random.default_rng(17))])
+    _compare(q, k, v, do, vec, _run(q, k, v, do, vec, dtype), dtype)
+
+
+@pytest.mark.parametrize("N", [1, 7, 64, 130])
+@pytest.mark.parametrize("d,dtype", WIDE)
+def test_small_and_ragged(d, dtype, N):
+    bf = dtype == torch.bfloat16
+    say(f"wide d={d} {dtype} ragged N={N}")
+    q, k, v, do = _inputs(1, 1, N, N, d, 8100, bf)
+    vec = I.stack_masks([I.make_mask("document", N, np.random.default_rng(5))])
+    _compare(q, k, v, do, vec, _run(q, k, v, do, vec, dtype), dtype)
+
+
+@pytest.mark.parametrize("d,dtype", WIDE)
+def test_sink_and_batches(d, dtype):
+    bf = dtype == torch.bfloat16
+    B, H, N = 2, 2, 333
+    say(f"wide d={d} {dtype} sink B={B}")
+    q, k, v, do = _inputs(B, H, N, N, d, 8200, bf)
+    vec = I.stack_masks([I.make_mask("share_question", N, np.random.default_rng(30 + b)) for b in range(B)])
+    sink = np.array([0.75, -1.25])
+    _compare(q, k, v, do, vec, _run(q, k, v, do, vec, dtype, sink=sink), dtype, sink=sink)
+
+
+@pytest.mark.parametrize("d,dtype", WIDE)
+def test_rectangular(d, dtype):
+    """Nq != Nk: 300 query rows against 700 keys, vectors over the keys."""
+    bf = dtype == torch.bfloat16
+    Nq, Nk = 300, 700
+    say(f"wide d={d} {dtype} Nq={Nq} Nk={Nk}")
+    q, k, v, do = _inputs(1, 2, Nq, Nk, d, 8300, bf)
+    rng = np.random.default_rng(3)
+    lts = rng.integers(0, Nq + 1, (1, 1, Nk)).astype(np.int32)
+    lte = np.minimum(lts + rng.integers(0, Nq // 2, (1, 1, Nk)), Nq).astype(np.int32)
+    uts = np.zeros((1, 1, Nk), np.int32)
+    ute = rng.integers(0, Nq // 8, (1, 1, Nk)).astype(np.int32)
+    vec = (lts, lte, uts, ute, False)
+    _compare(q, k, v, do, vec, _run(q, k, v, do, vec, dtype), dtype)
+
+
+@pytest.mark.parametrize("d,dtype", WIDE)
+def test_tile_counts_and_determinism(d, dtype):
+    """Tile counters at the reported tile shapes; every output repeats bitwise."""
+    bf = dtype == torch.bfloat16
+    B, H, N = 2, 2, 700
+    say(f"wide d={d} {dtype} tile counts and determinism")
+    q, k, v, do = _inputs(B, H, N, N, d, 8400, bf)
+    vec = I.stack_masks([I.make_mask("prefix_lm_document", N, np.random.default_rng(b)) for b in range(B)])
+    fc = torch.zeros(3, dtype=torch.int64, device="cuda")
+    bc = torch.zeros(3, dtype=torch.int64, device="cuda")
+    got1 = _run(q, k, v, do, vec, dtype, fcounts=fc, bcounts=bc)
+    got2 = _run(q, k, v, do, vec, dtype)
+    lts, lte, uts, ute, causal = vec
+    for is_bwd, counts in ((False, fc), (True, bc)):
+        bq, bk = fm.tile_shape(is_bwd, d, dtype)
+        t = oracle.kblock_minmax(B, 1, N, bk, lts, lte, uts, ute)
+        ref = oracle.classify_counts(oracle.classify(t, N, bq, bk, causal)) * H
+        assert counts.cpu().numpy().tolist() == ref.tolist(), (is_bwd, bq, bk)
+    for a, b in zip(got1, got2):
+        assert torch.equal(a, b)
+    _compare(q, k, v, do, vec, got1, dtype)
+
+
+@pytest.mark.parametrize("family", ["document", "causal"])
+def test_full_size_bf16_d512(family):
+    """B=1 H=4 N=8192 bf16 d = dv = 512: every output finite, whole heads 0
+    and 3 against the oracle."""
+    B, H, N, d = 1, 4, 8192, 512
+    say(f"wide full size d={d} family={family}")
+    q, k, v, do = _inputs(B, H, N, N, d, 8500, True)
+    vec = I.config_masks(5, family, n=N, batch=B)
+    got = _run(q, k, v, do, vec, torch.bfloat16)
+    for x in got:
+        assert bool((torch.isfinite(x) | torch.isneginf(x)).all())
+    _compare(q, k, v, do, vec, got, torch.bfloat16, heads=[(0, 0), (0, 3)])
