@@ -54,7 +54,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Both enums are int-sized. C++ fixes int as their underlying type, so any
+ * int a caller passes (an unknown status or dtype from C or a foreign-function
+ * binding) is a valid value to test and reject; C gives them int
+ * representation already. */
+#ifdef __cplusplus
+#define FM_ENUM_INT : int
+#else
+#define FM_ENUM_INT
+#endif
+
+typedef enum fm_status_e FM_ENUM_INT {
     FM_SUCCESS = 0,
     FM_ERROR_INVALID_VALUE = 1,       /* NULL required pointer, bad size, hm not in {1, H}, ... */
     FM_ERROR_NOT_SUPPORTED = 2,       /* (d, dv, dtype) combination not compiled in */
@@ -62,7 +72,7 @@ typedef enum {
     FM_ERROR_HIP = 4                  /* a kernel launch failed */
 } fm_status_t;
 
-typedef enum { FM_FP32 = 0, FM_BF16 = 1 } fm_dtype_t;
+typedef enum fm_dtype_e FM_ENUM_INT { FM_FP32 = 0, FM_BF16 = 1 } fm_dtype_t;
 
 /* Static text for a status code; never NULL. */
 const char* flashmask_status_string(fm_status_t status);
@@ -79,7 +89,9 @@ fm_status_t flashmask_tile_shape(int is_bwd, int d, fm_dtype_t dtype,
                                  int* block_q, int* block_k);
 
 /* Bytes of device workspace flashmask_fwd (is_bwd == 0) or flashmask_bwd
- * (is_bwd != 0) needs for these sizes; 0 on invalid sizes. The workspace
+ * (is_bwd != 0) needs for these sizes; 0 on invalid sizes (negative, hm not
+ * in {1, H}, dims not supported, or sizes the kernels cannot address, which
+ * flashmask_fwd/flashmask_bwd reject with FM_ERROR_NOT_SUPPORTED). The workspace
  * needs 256-byte alignment. It holds per-call state (the key-block table;
  * for the backward also delta, the base-2 logsumexp, the row sums of dS
  * the sink gradient uses and the work-queue counters of the dK/dV pass), so

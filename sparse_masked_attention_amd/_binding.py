@@ -8,6 +8,7 @@ no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -17,9 +18,12 @@ from typing import Optional
 import torch
 
 __all__ = ["FlashMaskError", "Mask", "lib", "status_string", "table_block", "tile_shape",
-           "workspace_size", "tile_classify", "fwd", "bwd", "localize", "max_chunks", "LIB_PATH"]
+           "workspace_size", "tile_classify", "fwd", "bwd", "localize", "max_chunks", "LIB_PATH",
+           "ALT_LIB_PATH", "library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libflashmask.so")
+# the second tile configuration (built alongside; see build.py)
+ALT_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libflashmask_alt.so")
 
 FM_FP32 = 0
 FM_BF16 = 1
@@ -66,19 +70,37 @@ class FlashMaskError(RuntimeError):
         self.status = status
 
 
+def _load(path: str):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m sparse_masked_attention_amd.build`")
+    handle = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
 def lib():
     """Load libflashmask.so once; raise if it is missing."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m sparse_masked_attention_amd.build`")
-        handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = handle
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Inside the block, every call of this module goes to the library at
+    ``path`` (same C ABI): the parity tests use it for the second tile
+    configuration, ALT_LIB_PATH."""
+    global _lib
+    saved = _lib
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
 
 
 def status_string(status: int) -> str:

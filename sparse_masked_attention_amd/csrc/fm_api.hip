@@ -46,6 +46,20 @@ size_t table_bytes(int B, int hm, int N) {
   return (size_t)B * hm * (size_t)ceil_div(N, kTableBlock) * 8 * sizeof(int32_t);
 }
 
+// Sizes the kernels can address (sizes already non-negative): 32-bit buffer
+// offsets cover one (batch, head) slice of a tensor, and B * H * ceil(rows /
+// 32) stays below 2^31 (32-row units index grids and queues). Each product
+// is formed only where it cannot overflow: B * H < 2^62 always, and once
+// below 2^31 it times ceil(rows / 32) < 2^26 stays below 2^57.
+bool addressable(int B, int H, int Nq, int Nk, int d, int dv, fm_dtype_t dtype) {
+  const long long lim = 1LL << 31;
+  const long long rows = Nq > Nk ? Nq : Nk;
+  const long long width = d > dv ? d : dv;
+  if (rows * width * (dtype == FM_BF16 ? 2 : 4) >= lim) return false;
+  const long long bh = (long long)B * H;
+  return bh < lim && bh * ceil_div(rows, 32) < lim;
+}
+
 // Checks shared by the attention entry points; FM_SUCCESS when usable.
 fm_status_t check_common(int B, int H, int Nq, int Nk, int d, int dv, fm_dtype_t dtype, int hm,
                          const int32_t* uts, const int32_t* ute, int causal) {
@@ -55,12 +69,7 @@ fm_status_t check_common(int B, int H, int Nq, int Nk, int d, int dv, fm_dtype_t
   if (H > 0 && hm != 1 && hm != H) return FM_ERROR_INVALID_VALUE;
   if (!causal && ((uts == nullptr) != (ute == nullptr))) return FM_ERROR_INVALID_VALUE;
   if (!supported(d, dv, dtype)) return FM_ERROR_NOT_SUPPORTED;
-  // 32-bit buffer offsets address one (batch, head) slice of a tensor
-  const long long rows = Nq > Nk ? Nq : Nk;
-  const long long width = d > dv ? d : dv;
-  if (rows * width * (dtype == FM_BF16 ? 2 : 4) >= (1LL << 31)) return FM_ERROR_NOT_SUPPORTED;
-  if ((long long)B * H * ceil_div(rows, 32) >= (1LL << 31)) return FM_ERROR_NOT_SUPPORTED;
-  return FM_SUCCESS;
+  return addressable(B, H, Nq, Nk, d, dv, dtype) ? FM_SUCCESS : FM_ERROR_NOT_SUPPORTED;
 }
 
 fm::MaskArgs mask_args(const int32_t* lts, const int32_t* lte, const int32_t* uts,
@@ -124,7 +133,8 @@ fm_status_t flashmask_tile_shape(int is_bwd, int d, fm_dtype_t dtype, int* block
 size_t flashmask_workspace_size_qk(int is_bwd, int B, int H, int Nq, int Nk, int d, int dv, int hm,
                                    fm_dtype_t dtype) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || hm <= 0 || d <= 0 || dv <= 0) return 0;
-  if (!supported(d, dv, dtype)) return 0;
+  if (H > 0 && hm != 1 && hm != H) return 0;
+  if (!supported(d, dv, dtype) || !addressable(B, H, Nq, Nk, d, dv, dtype)) return 0;
   size_t bytes = align_up(table_bytes(B, hm, Nk));
   if (is_bwd) {
     // delta, base-2 LSE, rowsum(dS), the dK/dV pass's work-queue counters

@@ -123,7 +123,11 @@ struct BwdCfg {
   static constexpr int NSPLIT = D >= 256 ? 2 : 1;
   static constexpr int DO = D / NSPLIT;         // dK columns per workgroup
   static constexpr int DVO = DV / NSPLIT;       // dV columns per workgroup
+#ifdef FM_ALT_TILES
+  static constexpr int BQ = 32;                 // query rows per step (second configuration)
+#else
   static constexpr int BQ = D > 128 ? 32 : 64;  // query rows per step
+#endif
   static constexpr int CHQ = D / 8;             // 16-byte chunks per Q row
   static constexpr int CHO = DV / 8;            // 16-byte chunks per dO row
   static constexpr int QT = BQ * D * 2;         // bytes of one Q tile

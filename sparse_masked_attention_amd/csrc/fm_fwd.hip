@@ -107,8 +107,13 @@ struct QCfg {
   static constexpr int WR = 32;                           // query rows per wave
   static constexpr int BR = WR * NW;                      // query rows per workgroup
   static constexpr int BC = 64;                           // keys per tile
-  // 32-key blocks per inner step (1 keeps registers within budget)
+  // 32-key blocks per inner step (1 keeps registers within budget; the
+  // second tile configuration, FM_ALT_TILES, takes 1 everywhere)
+#ifdef FM_ALT_TILES
+  static constexpr int JBS = 1;
+#else
   static constexpr int JBS = (D > 128 || DV > 128 || MODE != kModeFwd) ? 1 : 2;
+#endif
   // Forward with one wave per SIMD and room for both halves' scores (d = 192,
   // dv = 128): pipeline the tile's two 32-key halves within the wave. With
   // two waves per SIMD (d <= 128) the other wave already fills the MFMA pipe
@@ -122,7 +127,11 @@ struct QCfg {
   static constexpr int LOADS_V = VT / (NW * 1024);
   static constexpr int VEC = 4 * BC * 4;                  // the tile's boundary vectors
   static constexpr int STAGE = KT + VT + VEC;
+#ifdef FM_ALT_TILES
+  static constexpr int LIST = 2 * NW * 64;                // compacted tile list entries
+#else
   static constexpr int LIST = 1024;                       // compacted tile list entries
+#endif
   static constexpr int LOADS_PER_TILE = LOADS_K + LOADS_V + 1;  // waves 0-3 (they stage a vector)
   // two workgroups per CU when both fit in LDS and 256 registers
   static constexpr int WG_PER_CU = (D <= 128 && DV <= 128) ? 2 : 1;

@@ -15,8 +15,13 @@ constexpr int kFwdBlockK = 64;
 // forward query-block height: 4 waves x 32 rows for every head dim and dtype
 inline int fwd_block_q(int d, int is_bf16) { (void)d; (void)is_bf16; return 128; }
 constexpr int kBwdBlockK = 128;
-// backward query-block height: 64 rows for bf16 with d <= 128, else 32
+// backward query-block height: 64 rows for bf16 with d <= 128, else 32 (32
+// everywhere in the second tile configuration, FM_ALT_TILES)
+#ifdef FM_ALT_TILES
+inline int bwd_block_q(int d, int is_bf16) { (void)d; (void)is_bf16; return 32; }
+#else
 inline int bwd_block_q(int d, int is_bf16) { return (is_bf16 && d <= 128) ? 64 : 32; }
+#endif
 inline bool wide_dims(int d, int dv, bool is_bf16);
 // backward key-block width: 64 keys at the wide head dims, else kBwdBlockK
 inline int bwd_block_k(int d, int is_bf16) { return wide_dims(d, d, is_bf16 != 0) ? 64 : kBwdBlockK; }
