@@ -4,9 +4,11 @@ d = dv = 256 (the README lists large head dims among FlashMask's features,
 
 Forward and backward against the fp64 oracle on every mask family at
 N in {129, 1000}, ragged small N, a sink, Nq != Nk, the tile counters at
-the reported tile shapes, bitwise repeatability, and a full-size
-B=1 H=4 N=8192 case with whole-head checks on two heads (bf16). bf16 values
-follow the replay-aware rule of gpu_util.check_bf16; fp32 the fixed 1e-5.
+the reported tile shapes, bitwise repeatability, a full-size B=1 H=4
+N=8192 case with whole-head checks on two heads (bf16), and seeded random
+cases (batch, heads, per-head masks, Nq != Nk with arbitrary bounds, causal
+flag, sink). bf16 values follow the replay-aware rule of
+gpu_util.check_bf16; fp32 the fixed 1e-5.
 """
 import numpy as np
 import pytest
@@ -157,3 +159,41 @@ def test_full_size_bf16_d512(family):
     for x in got:
         assert bool((torch.isfinite(x) | torch.isneginf(x)).all())
     _compare(q, k, v, do, vec, got, torch.bfloat16, heads=[(0, 0), (0, 3)])
+
+
+def _draw(seed):
+    """A seeded random case at a wide head dim: dtype, B, H, per-head or
+    shared masks, Nq != Nk with arbitrary interval bounds or a mask family
+    with Nq = Nk, causal flag, sink."""
+    from test_gpu_random import FAMILIES as ALL_FAMILIES, family_bounds, random_bounds
+    rng = np.random.default_rng(70_000 + seed)
+    d, dtype = WIDE[int(rng.integers(0, len(WIDE)))]
+    B = int(rng.integers(1, 3))
+    H = int(rng.integers(1, 4))
+    hm = H if rng.random() < 0.4 else 1
+    nk = int(rng.integers(1, 520))
+    if rng.random() < 0.5:
+        nq = int(rng.integers(1, 2 * nk + 2))
+        causal = bool(rng.random() < 0.5)
+        lts, lte, uts, ute = random_bounds(rng, nq, nk, hm, B)
+        vec = (lts, lte, None, None, True) if causal else (lts, lte, uts, ute, False)
+        family = "random"
+    else:
+        nq = nk
+        family = ALL_FAMILIES[int(rng.integers(0, len(ALL_FAMILIES)))]
+        vec = family_bounds(rng, nk, hm, B, family)
+    sink = rng.normal(0.0, 2.0, H).astype(np.float32) if rng.random() < 0.3 else None
+    return d, dtype, B, H, hm, nq, nk, family, vec, sink
+
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_random_cases(seed):
+    d, dtype, B, H, hm, nq, nk, family, vec, sink = _draw(seed)
+    bf = dtype == torch.bfloat16
+    say(f"wide random seed={seed} d={d} {dtype} B={B} H={H} hm={hm} nq={nq} nk={nk} "
+        f"family={family} causal={vec[4]} sink={'yes' if sink is not None else 'no'}")
+    q = I.randn((B, H, nq, d), 71_000 + 4 * seed, bf16=bf)
+    k = I.randn((B, H, nk, d), 71_001 + 4 * seed, bf16=bf)
+    v = I.randn((B, H, nk, d), 71_002 + 4 * seed, bf16=bf)
+    do = I.randn((B, H, nq, d), 71_003 + 4 * seed, bf16=bf)
+    _compare(q, k, v, do, vec, _run(q, k, v, do, vec, dtype, sink=sink), dtype, sink=sink)
