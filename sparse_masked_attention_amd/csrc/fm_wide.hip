@@ -2,8 +2,8 @@
 //
 // The pages list large head dims among the method's features (FlashMask
 // README, "News" and "Key Features"); the computation is the same as at
-// the narrower dims (FlashMask paper, "Formulation": S = scale Q K^T plus
-// the column-wise mask bias, online softmax, P V; the backward's
+// the narrower dims (FlashMask README, "Formulation": S = scale Q K^T plus
+// the column-wise mask bias, softmax, P V; and its gradient, with
 // dS = P (dP - delta)), only the rows are wider.
 //
 // At these widths one row of Q, K, V or dO is 1 KiB, so a lane that keeps
@@ -15,12 +15,13 @@
 // workgroups of one tile's chunks each form its scores (and dP) again.
 // Tiles go through LDS with plain 16-byte loads, one stage, no pipelining.
 //
-// MFMA: v_mfma_f32_32x32x16_bf16 (bf16) and v_mfma_f32_32x32x2_f32 (fp32),
-// both with lane (n = lane % 32, k-group = lane / 32) operands and the
-// 32x32 accumulator layout in which lane (n, h) holds M index
-// 8 * (r / 4) + 4 * h + r % 4 in register r. A product whose contraction
-// runs over such an accumulator's M index (P V, dS K, P^T dO, dS^T Q)
-// takes the other operand's rows in that same order.
+// MFMA in the forward and dQ pass: v_mfma_f32_32x32x16_bf16 (bf16) and
+// v_mfma_f32_32x32x2_f32 (fp32), both with lane (n = lane % 32, k-group =
+// lane / 32) operands and the 32x32 accumulator layout in which lane (n, h)
+// holds M index 8 * (r / 4) + 4 * h + r % 4 in register r. A product whose
+// contraction runs over such an accumulator's M index (P V, dS K) takes the
+// other operand's rows in that same order. The dK/dV pass uses the 16x16
+// forms instead (its section says why and how).
 #include <type_traits>
 
 #include "fm_device.hpp"
