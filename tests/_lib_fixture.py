@@ -5,8 +5,9 @@ from sparse_masked_attention_amd import _binding
 
 
 def ensure_built():
-    """Build libflashmask.so only if it is missing (the GPU machine gets it prebuilt)."""
-    if not os.path.exists(_binding.LIB_PATH):
+    """Build the libraries (libflashmask.so and the second tile configuration,
+    libflashmask_alt.so) only if one is missing (the GPU machine gets them prebuilt)."""
+    if not (os.path.exists(_binding.LIB_PATH) and os.path.exists(_binding.ALT_LIB_PATH)):
         from sparse_masked_attention_amd import build
         build.build(verbose=False)
     return _binding.lib()
