@@ -42,7 +42,8 @@
  *   - Supported (forward and backward): dtype FM_BF16 with d == dv in
  *     {64, 128, 256, 512} or d = 192 with dv = 128 (Q/K head dim larger than
  *     V's; README "News" and "Key Features": large head dims); FM_FP32 with
- *     d == dv in {64, 128, 256}. Others: FM_ERROR_NOT_SUPPORTED.
+ *     d == dv in {64, 128, 256} or d = 192 with dv = 128. Others:
+ *     FM_ERROR_NOT_SUPPORTED.
  */
 #ifndef FLASHMASK_H
 #define FLASHMASK_H

@@ -25,8 +25,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
-// bf16: d = dv in {64, 128, 256} and (d, dv) = (192, 128); fp32: d = dv in
-// {64, 128}. Forward and backward cover the same set.
+// bf16: d = dv in {64, 128, 256, 512} and (d, dv) = (192, 128); fp32: d = dv
+// in {64, 128, 256} and (192, 128). Forward and backward cover the same set.
 bool supported(int d, int dv, fm_dtype_t dtype) {
   if (dtype == FM_BF16) return fm::bf16_dims(d, dv);
   if (dtype == FM_FP32) return fm::fp32_dims(d, dv);
@@ -36,9 +36,7 @@ bool supported(int d, int dv, fm_dtype_t dtype) {
 bool bwd_supported(int d, int dv, fm_dtype_t dtype) { return supported(d, dv, dtype); }
 
 // some dv makes (d, dv) supported: the tile shape depends on d only
-bool supported_d(int d, fm_dtype_t dtype) {
-  return supported(d, d, dtype) || (dtype == FM_BF16 && fm::bf16_dims(d, 128));
-}
+bool supported_d(int d, fm_dtype_t dtype) { return supported(d, d, dtype) || supported(d, 128, dtype); }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

@@ -1034,7 +1034,10 @@ static hipError_t launch_bwd_main(const AttnArgs& a, hipStream_t stream) {
   if (wide_dims(a.d, a.dv, a.is_bf16)) {
     // delta and the base-2 LSE, then the wide dQ and dK/dV passes
     p.nqb = (p.Nq + 31) / 32;
-    const hipError_t e = a.is_bf16 ? launch_pre<512, bf16>(p, stream) : launch_pre<256, float>(p, stream);
+    // (the preprocess reads rows of O and dO, dv wide)
+    const hipError_t e = a.is_bf16       ? launch_pre<512, bf16>(p, stream)
+                         : a.dv == 256 ? launch_pre<256, float>(p, stream)
+                                       : launch_pre<128, float>(p, stream);
     if (e != hipSuccess) return e;
     return launch_wide_bwd(a, stream);
   }

@@ -22,17 +22,25 @@ inline int bwd_block_q(int d, int is_bf16) { (void)d; (void)is_bf16; return 32; 
 #else
 inline int bwd_block_q(int d, int is_bf16) { return (is_bf16 && d <= 128) ? 64 : 32; }
 #endif
-inline bool wide_dims(int d, int dv, bool is_bf16);
-// backward key-block width: 64 keys at the wide head dims, else kBwdBlockK
-inline int bwd_block_k(int d, int is_bf16) { return wide_dims(d, d, is_bf16 != 0) ? 64 : kBwdBlockK; }
+// backward key-block width: 64 keys where the wide-head-dim kernels serve the
+// Q/K head dim d (bf16 512; fp32 256 and 192), else kBwdBlockK
+inline int bwd_block_k(int d, int is_bf16) {
+  return (is_bf16 ? d == 512 : (d == 256 || d == 192)) ? 64 : kBwdBlockK;
+}
 
 // Head dims with kernels compiled in: (d, dv) pairs for bf16, d == dv for fp32.
 inline bool bf16_dims(int d, int dv) {
   return (d == dv && (d == 64 || d == 128 || d == 256 || d == 512)) || (d == 192 && dv == 128);
 }
-inline bool fp32_dims(int d, int dv) { return d == dv && (d == 64 || d == 128 || d == 256); }
-// the wide head dims (bf16 d = dv = 512, fp32 d = dv = 256), served by fm_wide.hip
-inline bool wide_dims(int d, int dv, bool is_bf16) { return d == dv && d == (is_bf16 ? 512 : 256); }
+inline bool fp32_dims(int d, int dv) {
+  return (d == dv && (d == 64 || d == 128 || d == 256)) || (d == 192 && dv == 128);
+}
+// the shapes served by the wide-head-dim kernels of fm_wide.hip: bf16
+// d = dv = 512; fp32 d = dv = 256 and (d, dv) = (192, 128)
+inline bool wide_dims(int d, int dv, bool is_bf16) {
+  if (is_bf16) return d == 512 && dv == 512;
+  return (d == 256 && dv == 256) || (d == 192 && dv == 128);
+}
 
 struct MaskArgs {
   const int32_t* lts;  // [B, hm, Nk] or nullptr

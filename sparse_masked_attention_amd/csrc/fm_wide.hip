@@ -527,18 +527,21 @@ __device__ inline typename W16<T>::op acc_op16(const f32x4 (&a)[2], int s) {
   }
 }
 
-// Workgroup: 64 keys (16 per wave), dK and dV columns [ch KCH, (ch + 1) KCH).
+// Workgroup: 64 keys (16 per wave), chunk ch of NCH: dK columns
+// [ch KCK, (ch + 1) KCK) and dV columns [ch KCV, (ch + 1) KCV), KCK = D / NCH,
+// KCV = DV / NCH.
 // K and V rows of the lane's key in registers; per visible 32-row query
 // step (Q, dO, LSE2 and delta in LDS):
 //   S = Q K^T, dP = dO V^T, the mask from the key's own bounds,
 //   P = exp2(S scale log2e - LSE2), dS = P (dP - delta),
 //   dV^T += dO^T P and dK^T += Q^T dS (this chunk's columns; dK takes the
 //   scale once, at the end).
-template <typename T, int D, int DV, int KCH>
+template <typename T, int D, int DV, int NCH>
 __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
   using X = W16<T>;
-  static_assert(D == DV, "one column chunk covers both dK and dV");
-  constexpr int KW = 16, BKC = 64, BQ = 32, NCH = D / KCH, KC = X::KC;
+  constexpr int KCK = D / NCH, KCV = DV / NCH;
+  static_assert(KCK * NCH == D && KCV * NCH == DV && KCK % 16 == 0 && KCV % 16 == 0, "column chunks");
+  constexpr int KW = 16, BKC = 64, BQ = 32, KC = X::KC;
   constexpr int QS = lds_stride<T, D>(), OS = lds_stride<T, DV>();
   __shared__ __attribute__((aligned(16))) T qs_[BQ * QS];
   __shared__ __attribute__((aligned(16))) T dos_[BQ * OS];
@@ -578,9 +581,15 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
     for (int c = 0; c < D / KC; ++c) {
       if constexpr (std::is_same<T, float>::value) {
         kr[c] = ok ? kg[(long long)j * D + 4 * c + g] : 0.f;
-        vr[c] = ok ? vg[(long long)j * DV + 4 * c + g] : 0.f;
       } else {
         kr[c] = ok ? *reinterpret_cast<const bf16x8*>(kg + (long long)j * D + 32 * c + 8 * g) : bf16x8{};
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < DV / KC; ++c) {
+      if constexpr (std::is_same<T, float>::value) {
+        vr[c] = ok ? vg[(long long)j * DV + 4 * c + g] : 0.f;
+      } else {
         vr[c] = ok ? *reinterpret_cast<const bf16x8*>(vg + (long long)j * DV + 32 * c + 8 * g) : bf16x8{};
       }
     }
@@ -597,12 +606,12 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
       k_ute = p.ute[vrow + j];
     }
   }
-  f32x4 dkacc[KCH / 16], dvacc[KCH / 16];
+  constexpr int NKB = KCK / 16, NVB = KCV / 16;   // 16-column blocks of the chunk
+  f32x4 dkacc[NKB], dvacc[NVB];
 #pragma unroll
-  for (int mb = 0; mb < KCH / 16; ++mb) {
-    dkacc[mb] = f32x4{};
-    dvacc[mb] = f32x4{};
-  }
+  for (int mb = 0; mb < NKB; ++mb) dkacc[mb] = f32x4{};
+#pragma unroll
+  for (int mb = 0; mb < NVB; ++mb) dvacc[mb] = f32x4{};
   // bounds of the workgroup's 64 keys (one table entry); a wave's 16 keys
   // lie inside them, so the same bounds classify its part (possibly as
   // partial where its own keys alone would not be)
@@ -633,17 +642,24 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
     __syncthreads();
     if (wc == 0) continue;
     // S = Q K^T and dP = dO V^T for the step's two 16-row halves (lane:
-    // key j; rows 16 mt + 4 g + e)
+    // key j; rows 16 mt + 4 g + e); the two chains alternate while both
+    // have steps left (D / KC and DV / KC of them)
+    constexpr int NSS = D / KC, NSD = DV / KC, NSMIN = NSS < NSD ? NSS : NSD;
+    auto is_dp = [](int t) { return t < 2 * NSMIN ? (t & 1) != 0 : NSD > NSS; };
+    auto sstep = [](int t) { return t < 2 * NSMIN ? t >> 1 : t - NSMIN; };
     f32x4 s[2], dp[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       s[mt] = f32x4{};
       dp[mt] = f32x4{};
-      chain<2 * (D / KC), 2>(
-          [&](int t) { return row_op16<T>((t & 1) ? dos : qs, (t & 1) ? OS : QS, 16 * mt + n16, t >> 1, g); },
+      chain<NSS + NSD, 2>(
+          [&](int t) {
+            return is_dp(t) ? row_op16<T>(dos, OS, 16 * mt + n16, sstep(t), g)
+                            : row_op16<T>(qs, QS, 16 * mt + n16, sstep(t), g);
+          },
           [&](int t, typename X::op a) {
-            if (t & 1) dp[mt] = X::mma(a, vr[t >> 1], dp[mt]);
-            else s[mt] = X::mma(a, kr[t >> 1], s[mt]);
+            if (is_dp(t)) dp[mt] = X::mma(a, vr[sstep(t)], dp[mt]);
+            else s[mt] = X::mma(a, kr[sstep(t)], s[mt]);
           });
     }
 #pragma unroll
@@ -659,6 +675,8 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
       }
     // P and dS as operands once (bf16: rounded), then dV^T += dO^T P and
     // dK^T += Q^T dS over the step's 32 rows, the two products alternating
+    // while both have steps left; step u of a product is column block
+    // u / NST, row step u % NST
     constexpr int NST = 32 / KC;
     typename X::op pop[NST], dsop[NST];
 #pragma unroll
@@ -666,35 +684,45 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
       pop[st] = acc_op16<T>(s, st);
       dsop[st] = acc_op16<T>(dp, st);
     }
-    chain<2 * (KCH / 16) * NST, 2>(
+    constexpr int NMIN = (NKB < NVB ? NKB : NVB) * NST;
+    auto is_k = [](int t) { return t < 2 * NMIN ? (t & 1) != 0 : NKB > NVB; };
+    auto step_of = [](int t) { return t < 2 * NMIN ? t >> 1 : t - NMIN; };
+    chain<(NKB + NVB) * NST, 2>(
         [&](int t) {
-          const int mb = t / (2 * NST), st = (t / 2) % NST;
-          return col_op16<T>((t & 1) ? qs : dos, (t & 1) ? QS : OS, ch * KCH + 16 * mb + n16, st, g);
+          const int u = step_of(t), mb = u / NST, st = u % NST;
+          return is_k(t) ? col_op16<T>(qs, QS, ch * KCK + 16 * mb + n16, st, g)
+                         : col_op16<T>(dos, OS, ch * KCV + 16 * mb + n16, st, g);
         },
         [&](int t, typename X::op a) {
-          const int mb = t / (2 * NST), st = (t / 2) % NST;
-          if (t & 1) dkacc[mb] = X::mma(a, dsop[st], dkacc[mb]);
+          const int u = step_of(t), mb = u / NST, st = u % NST;
+          if (is_k(t)) dkacc[mb] = X::mma(a, dsop[st], dkacc[mb]);
           else dvacc[mb] = X::mma(a, pop[st], dvacc[mb]);
         });
   }
 
-  // lane: key j, columns ch KCH + 16 mb + 4 g + e
+  // lane: key j, dK columns ch KCK + 16 mb + 4 g + e, dV columns ch KCV + ...
   if (j < Nk) {
-    T* dkg = reinterpret_cast<T*>(p.dk) + (kslice + j) * D + ch * KCH;
-    T* dvg = reinterpret_cast<T*>(p.dv) + (kslice + j) * DV + ch * KCH;
+    T* dkg = reinterpret_cast<T*>(p.dk) + (kslice + j) * D + ch * KCK;
+    T* dvg = reinterpret_cast<T*>(p.dv) + (kslice + j) * DV + ch * KCV;
 #pragma unroll
-    for (int mb = 0; mb < KCH / 16; ++mb) {
+    for (int mb = 0; mb < NKB; ++mb) {
       if constexpr (std::is_same<T, float>::value) {
         *reinterpret_cast<f32x4*>(dkg + 16 * mb + 4 * g) = dkacc[mb] * p.scale;
+      } else {
+        bf16x4 k4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) k4[e] = (bf16)(dkacc[mb][e] * p.scale);
+        *reinterpret_cast<bf16x4*>(dkg + 16 * mb + 4 * g) = k4;
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < NVB; ++mb) {
+      if constexpr (std::is_same<T, float>::value) {
         *reinterpret_cast<f32x4*>(dvg + 16 * mb + 4 * g) = dvacc[mb];
       } else {
-        bf16x4 k4, v4;
+        bf16x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k4[e] = (bf16)(dkacc[mb][e] * p.scale);
-          v4[e] = (bf16)dvacc[mb][e];
-        }
-        *reinterpret_cast<bf16x4*>(dkg + 16 * mb + 4 * g) = k4;
+        for (int e = 0; e < 4; ++e) v4[e] = (bf16)dvacc[mb][e];
         *reinterpret_cast<bf16x4*>(dvg + 16 * mb + 4 * g) = v4;
       }
     }
@@ -707,17 +735,21 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
 }
 
 // ---------------------------------------------------------------- launch
-// Column chunks per head dim and dtype: the forward's O chunk, the dQ
-// pass's dQ chunk and the dK/dV pass's chunk of both.
-template <typename T>
+// Column chunks per shape: the forward's O chunk (DVC columns), the dQ
+// pass's dQ chunk (DC) and the number of dK/dV chunks (NCH).
+template <typename T, int D, int DV>
 struct WideCfg;
 template <>
-struct WideCfg<float> {   // d = dv = 256
-  static constexpr int D = 256, DVC = 256, DC = 128, KCH = 256;
+struct WideCfg<bf16, 512, 512> {
+  static constexpr int DVC = 256, DC = 128, NCH = 2;
 };
 template <>
-struct WideCfg<bf16> {    // d = dv = 512
-  static constexpr int D = 512, DVC = 256, DC = 128, KCH = 256;
+struct WideCfg<float, 256, 256> {
+  static constexpr int DVC = 256, DC = 128, NCH = 1;
+};
+template <>
+struct WideCfg<float, 192, 128> {
+  static constexpr int DVC = 128, DC = 192, NCH = 1;
 };
 
 static WideParams wide_params(const AttnArgs& a) {
@@ -755,40 +787,45 @@ static WideParams wide_params(const AttnArgs& a) {
   return p;
 }
 
-template <typename T>
+template <typename T, int D, int DV>
 static hipError_t launch_wide_fwd_t(const AttnArgs& a, hipStream_t stream) {
-  using C = WideCfg<T>;
+  using C = WideCfg<T, D, DV>;
   WideParams p = wide_params(a);
   p.nqb = (a.Nq + 127) / 128;
-  const long long grid = (long long)a.B * a.H * p.nqb * (C::D / C::DVC);
-  hipLaunchKernelGGL((wide_fwd_kernel<T, C::D, C::D, C::DVC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  const long long grid = (long long)a.B * a.H * p.nqb * (DV / C::DVC);
+  hipLaunchKernelGGL((wide_fwd_kernel<T, D, DV, C::DVC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int D, int DV>
 static hipError_t launch_wide_bwd_t(const AttnArgs& a, hipStream_t stream) {
-  using C = WideCfg<T>;
+  using C = WideCfg<T, D, DV>;
   WideParams p = wide_params(a);
   p.pdsum = a.sink != nullptr ? a.pdsum : nullptr;
   p.nqb = (a.Nq + 127) / 128;
-  long long grid = (long long)a.B * a.H * p.nqb * (C::D / C::DC);
-  hipLaunchKernelGGL((wide_dq_kernel<T, C::D, C::D, C::DC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  long long grid = (long long)a.B * a.H * p.nqb * (D / C::DC);
+  hipLaunchKernelGGL((wide_dq_kernel<T, D, DV, C::DC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   p.nqb = (a.Nq + 31) / 32;
-  grid = (long long)a.B * a.H * p.nkb64 * (C::D / C::KCH);
-  hipLaunchKernelGGL((wide_dkdv_kernel<T, C::D, C::D, C::KCH>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  grid = (long long)a.B * a.H * p.nkb64 * C::NCH;
+  hipLaunchKernelGGL((wide_dkdv_kernel<T, D, DV, C::NCH>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
+// the shapes compiled in (kept in step with wide_dims())
 hipError_t launch_wide_fwd(const AttnArgs& a, hipStream_t stream) {
-  if (!wide_dims(a.d, a.dv, a.is_bf16)) return hipErrorInvalidValue;
-  return a.is_bf16 ? launch_wide_fwd_t<bf16>(a, stream) : launch_wide_fwd_t<float>(a, stream);
+  if (a.is_bf16 && a.d == 512 && a.dv == 512) return launch_wide_fwd_t<bf16, 512, 512>(a, stream);
+  if (!a.is_bf16 && a.d == 256 && a.dv == 256) return launch_wide_fwd_t<float, 256, 256>(a, stream);
+  if (!a.is_bf16 && a.d == 192 && a.dv == 128) return launch_wide_fwd_t<float, 192, 128>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_wide_bwd(const AttnArgs& a, hipStream_t stream) {
-  if (!wide_dims(a.d, a.dv, a.is_bf16)) return hipErrorInvalidValue;
-  return a.is_bf16 ? launch_wide_bwd_t<bf16>(a, stream) : launch_wide_bwd_t<float>(a, stream);
+  if (a.is_bf16 && a.d == 512 && a.dv == 512) return launch_wide_bwd_t<bf16, 512, 512>(a, stream);
+  if (!a.is_bf16 && a.d == 256 && a.dv == 256) return launch_wide_bwd_t<float, 256, 256>(a, stream);
+  if (!a.is_bf16 && a.d == 192 && a.dv == 128) return launch_wide_bwd_t<float, 192, 128>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fm

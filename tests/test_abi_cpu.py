@@ -60,9 +60,11 @@ def test_table_block_and_tile_shapes(lib):
     assert _binding.tile_shape(True, 128, torch.bfloat16) == (64, 128)
     assert _binding.tile_shape(True, 256, torch.bfloat16) == (32, 128)
     assert _binding.tile_shape(True, 64, torch.float32) == (32, 128)
-    # d = 192 exists for bf16 (with dv = 128) only
+    # d = 192 exists with dv = 128: bf16 (the narrower kernels) and fp32 (the wide ones)
     assert _binding.tile_shape(False, 192, torch.bfloat16) == (128, 64)
     assert _binding.tile_shape(True, 192, torch.bfloat16) == (32, 128)
+    assert _binding.tile_shape(False, 192, torch.float32) == (128, 64)
+    assert _binding.tile_shape(True, 192, torch.float32) == (32, 64)
     # the wide head dims: 64-key backward blocks
     assert _binding.tile_shape(False, 512, torch.bfloat16) == (128, 64)
     assert _binding.tile_shape(True, 512, torch.bfloat16) == (32, 64)
@@ -71,7 +73,7 @@ def test_table_block_and_tile_shapes(lib):
     with pytest.raises(_binding.FlashMaskError):
         _binding.tile_shape(False, 96, torch.bfloat16)
     with pytest.raises(_binding.FlashMaskError):
-        _binding.tile_shape(True, 192, torch.float32)
+        _binding.tile_shape(True, 512, torch.float32)
 
 
 def test_workspace_size(lib):
@@ -86,10 +88,11 @@ def test_workspace_size(lib):
     bwd32 = _binding.workspace_size(True, 1, 32, 8192, 128, 128, 1, torch.float32)
     assert bwd32 == bwd
     assert _binding.workspace_size(False, 1, 1, 10, 96, 96, 1, torch.bfloat16) == 0
-    # (d, dv) = (192, 128) for bf16 only; the workspace does not depend on dv
+    # (d, dv) = (192, 128) for bf16 and fp32; the workspace does not depend on dv
     assert _binding.workspace_size(True, 1, 32, 8192, 192, 128, 1, torch.bfloat16) == bwd
     assert _binding.workspace_size(True, 1, 32, 8192, 192, 192, 1, torch.bfloat16) == 0
-    assert _binding.workspace_size(True, 1, 32, 8192, 192, 128, 1, torch.float32) == 0
+    assert _binding.workspace_size(True, 1, 32, 8192, 192, 128, 1, torch.float32) == bwd32
+    assert _binding.workspace_size(True, 1, 32, 8192, 192, 192, 1, torch.float32) == 0
 
 
 def _fwd_call(lib, q=1, k=1, v=1, o=1, lse=1, hm=1, B=1, H=2, N=16, d=128, dv=128,
@@ -109,7 +112,7 @@ def test_fwd_argument_checks(lib):
     assert _fwd_call(lib, d=128, dv=64) == FM_NOT_SUPPORTED
     assert _fwd_call(lib, d=192, dv=192) == FM_NOT_SUPPORTED
     assert _fwd_call(lib, d=128, dv=192) == FM_NOT_SUPPORTED
-    assert _fwd_call(lib, dtype=0, d=192, dv=128) == FM_NOT_SUPPORTED
+    assert _fwd_call(lib, dtype=0, d=192, dv=192) == FM_NOT_SUPPORTED
     assert _fwd_call(lib, dtype=0, d=512, dv=512) == FM_NOT_SUPPORTED
     assert _fwd_call(lib, d=512, dv=256) == FM_NOT_SUPPORTED
     assert _fwd_call(lib, d=384, dv=384) == FM_NOT_SUPPORTED

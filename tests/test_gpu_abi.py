@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 PAD = 4096          # guard elements on each side (keeps 16-byte alignment)
 GUARD = 7.0         # guard value (exact in bf16 and fp32)
 BF16_DIMS = [(64, 64), (128, 128), (256, 256), (192, 128), (512, 512)]
-FP32_DIMS = [(64, 64), (128, 128), (256, 256)]
+FP32_DIMS = [(64, 64), (128, 128), (256, 256), (192, 128)]
 
 
 @pytest.fixture(scope="module", autouse=True)

@@ -1,6 +1,8 @@
-"""Parity at the wide head dims: bf16 with d = dv = 512 and fp32 with
-d = dv = 256 (the README lists large head dims among FlashMask's features,
-"News" and "Key Features"; the scale stays 1/sqrt(d), "Formulation").
+"""Parity at the shapes the wide-head-dim kernels serve: bf16 with
+d = dv = 512, fp32 with d = dv = 256 and with (d, dv) = (192, 128) (the
+README lists large head dims among FlashMask's features, "News" and "Key
+Features", with Q/K and V head dims apart; the scale stays 1/sqrt(d),
+"Formulation").
 
 Forward and backward against the fp64 oracle on every mask family at
 N in {129, 1000}, ragged small N, a sink, Nq != Nk, the tile counters at
@@ -23,7 +25,7 @@ from _lib_fixture import ensure_built
 
 pytestmark = pytest.mark.gpu
 
-WIDE = [(512, torch.bfloat16), (256, torch.float32)]
+WIDE = [(512, 512, torch.bfloat16), (256, 256, torch.float32), (192, 128, torch.float32)]
 FAMILIES = ["causal", "document", "share_question", "sliding_window", "block_sparse",
             "prefix_lm_document", "all_open"]
 
@@ -33,11 +35,11 @@ def _lib():
     ensure_built()
 
 
-def _inputs(B, H, Nq, Nk, d, seed, bf):
+def _inputs(B, H, Nq, Nk, d, dv, seed, bf):
     q = I.randn((B, H, Nq, d), seed, bf16=bf)
     k = I.randn((B, H, Nk, d), seed + 1, bf16=bf)
-    v = I.randn((B, H, Nk, d), seed + 2, bf16=bf)
-    do = I.randn((B, H, Nq, d), seed + 3, bf16=bf)
+    v = I.randn((B, H, Nk, dv), seed + 2, bf16=bf)
+    do = I.randn((B, H, Nq, dv), seed + 3, bf16=bf)
     return q, k, v, do
 
 
@@ -78,43 +80,43 @@ def _compare(q, k, v, do, vec, got, dtype, sink=None, heads=None):
 
 @pytest.mark.parametrize("family", FAMILIES)
 @pytest.mark.parametrize("N", [129, 1000])
-@pytest.mark.parametrize("d,dtype", WIDE)
-def test_families(d, dtype, family, N):
+@pytest.mark.parametrize("d,dv,dtype", WIDE)
+def test_families(d, dv, dtype, family, N):
     bf = dtype == torch.bfloat16
-    say(f"wide d={d} {dtype} family={family} N={N}")
-    q, k, v, do = _inputs(1, 2, N, N, d, 8000, bf)
+    say(f"wide d={d} dv={dv} {dtype} family={family} N={N}")
+    q, k, v, do = _inputs(1, 2, N, N, d, dv, 8000, bf)
     vec = I.stack_masks([I.make_mask(family, N, np.random.default_rng(17))])
     _compare(q, k, v, do, vec, _run(q, k, v, do, vec, dtype), dtype)
 
 
 @pytest.mark.parametrize("N", [1, 7, 64, 130])
-@pytest.mark.parametrize("d,dtype", WIDE)
-def test_small_and_ragged(d, dtype, N):
+@pytest.mark.parametrize("d,dv,dtype", WIDE)
+def test_small_and_ragged(d, dv, dtype, N):
     bf = dtype == torch.bfloat16
-    say(f"wide d={d} {dtype} ragged N={N}")
-    q, k, v, do = _inputs(1, 1, N, N, d, 8100, bf)
+    say(f"wide d={d} dv={dv} {dtype} ragged N={N}")
+    q, k, v, do = _inputs(1, 1, N, N, d, dv, 8100, bf)
     vec = I.stack_masks([I.make_mask("document", N, np.random.default_rng(5))])
     _compare(q, k, v, do, vec, _run(q, k, v, do, vec, dtype), dtype)
 
 
-@pytest.mark.parametrize("d,dtype", WIDE)
-def test_sink_and_batches(d, dtype):
+@pytest.mark.parametrize("d,dv,dtype", WIDE)
+def test_sink_and_batches(d, dv, dtype):
     bf = dtype == torch.bfloat16
     B, H, N = 2, 2, 333
-    say(f"wide d={d} {dtype} sink B={B}")
-    q, k, v, do = _inputs(B, H, N, N, d, 8200, bf)
+    say(f"wide d={d} dv={dv} {dtype} sink B={B}")
+    q, k, v, do = _inputs(B, H, N, N, d, dv, 8200, bf)
     vec = I.stack_masks([I.make_mask("share_question", N, np.random.default_rng(30 + b)) for b in range(B)])
     sink = np.array([0.75, -1.25])
     _compare(q, k, v, do, vec, _run(q, k, v, do, vec, dtype, sink=sink), dtype, sink=sink)
 
 
-@pytest.mark.parametrize("d,dtype", WIDE)
-def test_rectangular(d, dtype):
+@pytest.mark.parametrize("d,dv,dtype", WIDE)
+def test_rectangular(d, dv, dtype):
     """Nq != Nk: 300 query rows against 700 keys, vectors over the keys."""
     bf = dtype == torch.bfloat16
     Nq, Nk = 300, 700
-    say(f"wide d={d} {dtype} Nq={Nq} Nk={Nk}")
-    q, k, v, do = _inputs(1, 2, Nq, Nk, d, 8300, bf)
+    say(f"wide d={d} dv={dv} {dtype} Nq={Nq} Nk={Nk}")
+    q, k, v, do = _inputs(1, 2, Nq, Nk, d, dv, 8300, bf)
     rng = np.random.default_rng(3)
     lts = rng.integers(0, Nq + 1, (1, 1, Nk)).astype(np.int32)
     lte = np.minimum(lts + rng.integers(0, Nq // 2, (1, 1, Nk)), Nq).astype(np.int32)
@@ -124,13 +126,13 @@ def test_rectangular(d, dtype):
     _compare(q, k, v, do, vec, _run(q, k, v, do, vec, dtype), dtype)
 
 
-@pytest.mark.parametrize("d,dtype", WIDE)
-def test_tile_counts_and_determinism(d, dtype):
+@pytest.mark.parametrize("d,dv,dtype", WIDE)
+def test_tile_counts_and_determinism(d, dv, dtype):
     """Tile counters at the reported tile shapes; every output repeats bitwise."""
     bf = dtype == torch.bfloat16
     B, H, N = 2, 2, 700
-    say(f"wide d={d} {dtype} tile counts and determinism")
-    q, k, v, do = _inputs(B, H, N, N, d, 8400, bf)
+    say(f"wide d={d} dv={dv} {dtype} tile counts and determinism")
+    q, k, v, do = _inputs(B, H, N, N, d, dv, 8400, bf)
     vec = I.stack_masks([I.make_mask("prefix_lm_document", N, np.random.default_rng(b)) for b in range(B)])
     fc = torch.zeros(3, dtype=torch.int64, device="cuda")
     bc = torch.zeros(3, dtype=torch.int64, device="cuda")
@@ -153,7 +155,7 @@ def test_full_size_bf16_d512(family):
     and 3 against the oracle."""
     B, H, N, d = 1, 4, 8192, 512
     say(f"wide full size d={d} family={family}")
-    q, k, v, do = _inputs(B, H, N, N, d, 8500, True)
+    q, k, v, do = _inputs(B, H, N, N, d, d, 8500, True)
     vec = I.config_masks(5, family, n=N, batch=B)
     got = _run(q, k, v, do, vec, torch.bfloat16)
     for x in got:
@@ -167,7 +169,7 @@ def _draw(seed):
     with Nq = Nk, causal flag, sink."""
     from test_gpu_random import FAMILIES as ALL_FAMILIES, family_bounds, random_bounds
     rng = np.random.default_rng(70_000 + seed)
-    d, dtype = WIDE[int(rng.integers(0, len(WIDE)))]
+    d, dv, dtype = WIDE[int(rng.integers(0, len(WIDE)))]
     B = int(rng.integers(1, 3))
     H = int(rng.integers(1, 4))
     hm = H if rng.random() < 0.4 else 1
@@ -183,17 +185,17 @@ def _draw(seed):
         family = ALL_FAMILIES[int(rng.integers(0, len(ALL_FAMILIES)))]
         vec = family_bounds(rng, nk, hm, B, family)
     sink = rng.normal(0.0, 2.0, H).astype(np.float32) if rng.random() < 0.3 else None
-    return d, dtype, B, H, hm, nq, nk, family, vec, sink
+    return d, dv, dtype, B, H, hm, nq, nk, family, vec, sink
 
 
-@pytest.mark.parametrize("seed", list(range(8)))
+@pytest.mark.parametrize("seed", list(range(10)))
 def test_random_cases(seed):
-    d, dtype, B, H, hm, nq, nk, family, vec, sink = _draw(seed)
+    d, dv, dtype, B, H, hm, nq, nk, family, vec, sink = _draw(seed)
     bf = dtype == torch.bfloat16
-    say(f"wide random seed={seed} d={d} {dtype} B={B} H={H} hm={hm} nq={nq} nk={nk} "
+    say(f"wide random seed={seed} d={d} dv={dv} {dtype} B={B} H={H} hm={hm} nq={nq} nk={nk} "
         f"family={family} causal={vec[4]} sink={'yes' if sink is not None else 'no'}")
     q = I.randn((B, H, nq, d), 71_000 + 4 * seed, bf16=bf)
     k = I.randn((B, H, nk, d), 71_001 + 4 * seed, bf16=bf)
-    v = I.randn((B, H, nk, d), 71_002 + 4 * seed, bf16=bf)
-    do = I.randn((B, H, nq, d), 71_003 + 4 * seed, bf16=bf)
+    v = I.randn((B, H, nk, dv), 71_002 + 4 * seed, bf16=bf)
+    do = I.randn((B, H, nq, dv), 71_003 + 4 * seed, bf16=bf)
     _compare(q, k, v, do, vec, _run(q, k, v, do, vec, dtype, sink=sink), dtype, sink=sink)
