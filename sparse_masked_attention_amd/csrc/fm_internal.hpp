@@ -12,8 +12,11 @@ constexpr int kTableBlock = 64;
 
 // Tile shapes the attention kernels classify (query rows x key columns).
 constexpr int kFwdBlockK = 64;
-// forward query-block height: 4 waves x 32 rows for every head dim and dtype
-inline int fwd_block_q(int d, int is_bf16) { (void)d; (void)is_bf16; return 128; }
+// forward query-block height: 4 waves x 32 rows, or 4 x 16 where the
+// wide-head-dim kernels serve the Q/K head dim d (bf16 512; fp32 256 and 192)
+inline int fwd_block_q(int d, int is_bf16) {
+  return (is_bf16 ? d == 512 : (d == 256 || d == 192)) ? 64 : 128;
+}
 constexpr int kBwdBlockK = 128;
 // backward query-block height: 64 rows for bf16 with d <= 128, else 32 (32
 // everywhere in the second tile configuration, FM_ALT_TILES)

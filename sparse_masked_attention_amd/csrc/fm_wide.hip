@@ -1,4 +1,5 @@
-// Wide head dims: bf16 with d = dv = 512 and fp32 with d = dv = 256.
+// Wide head dims: bf16 with d = dv = 512, fp32 with d = dv = 256 and with
+// (d, dv) = (192, 128).
 //
 // The pages list large head dims among the method's features (FlashMask
 // README, "News" and "Key Features"); the computation is the same as at
@@ -6,22 +7,25 @@
 // the column-wise mask bias, softmax, P V; and its gradient, with
 // dS = P (dP - delta)), only the rows are wider.
 //
-// At these widths one row of Q, K, V or dO is 1 KiB, so a lane that keeps
-// its row as MFMA operands spends 128 registers on it (of 512 at one wave
-// per SIMD). The kernels keep the decomposition of the narrower ones
-// (query-major forward and dQ pass, key-major dK/dV pass, the same per-tile
-// classification from the key-block table) and bound their accumulators by
-// splitting the output columns into chunks, one workgroup per chunk; the
-// workgroups of one tile's chunks each form its scores (and dP) again.
-// Tiles go through LDS with plain 16-byte loads, one stage, no pipelining.
+// Every product here uses the 16x16 MFMA forms (v_mfma_f32_16x16x32_bf16,
+// v_mfma_f32_16x16x4_f32): lane (n = lane % 16, k-group g = lane / 16)
+// operands, and a 16x16 accumulator in which lane (n, g) holds M index
+// 4 g + e in register e. With 16 rows (or keys) per wave a lane keeps a
+// quarter of its row of Q and dO (or K and V) as operands, 64 registers at
+// 1 KiB rows, so a whole output row fits in accumulators: each tile's
+// scores are formed once, with no split of the output columns.
 //
-// MFMA in the forward and dQ pass: v_mfma_f32_32x32x16_bf16 (bf16) and
-// v_mfma_f32_32x32x2_f32 (fp32), both with lane (n = lane % 32, k-group =
-// lane / 32) operands and the 32x32 accumulator layout in which lane (n, h)
-// holds M index 8 * (r / 4) + 4 * h + r % 4 in register r. A product whose
-// contraction runs over such an accumulator's M index (P V, dS K) takes the
-// other operand's rows in that same order. The dK/dV pass uses the 16x16
-// forms instead (its section says why and how).
+// Contractions over a tile's rows (P V, dS K, P^T dO, dS^T Q) take the
+// other operand in the order of the score accumulators: element e of lane
+// group g is tile row 16 (e / 4) + 4 g + e % 4. bf16 reads such a column
+// block with two transposed LDS reads (ds_read_b64_tr_b16), fp32 with one
+// float per MFMA step.
+//
+// The three kernels keep the decomposition of the narrower ones (query-major
+// forward and dQ pass, key-major dK/dV pass, each tile classified from the
+// key-block table). Tiles of 32 rows move into LDS by LDS DMA (one 16-byte
+// piece per lane, one instruction per tile row), two stages deep: the next
+// visible tile loads while the current one is computed.
 #include <type_traits>
 
 #include "fm_device.hpp"
@@ -54,80 +58,78 @@ struct WideParams {
   int nqb, nkb64;   // query blocks (or steps); 64-key table entries
 };
 
-// ---------------------------------------------------------------- element types
+// ---------------------------------------------------------------- MFMA forms
 template <typename T>
-struct Wt;
+struct W16;
 template <>
-struct Wt<float> {
+struct W16<float> {
   using op = float;
-  static constexpr int KC = 2;   // contraction depth of one MFMA
-  __device__ static f32x16 mma(float a, float b, f32x16 c) { return mfma32f(a, b, c); }
+  static constexpr int KC = 4;   // contraction depth of one MFMA
+  __device__ static f32x4 mma(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
 };
 template <>
-struct Wt<bf16> {
+struct W16<bf16> {
   using op = bf16x8;
-  static constexpr int KC = 16;
-  __device__ static f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) { return mfma32(a, b, c); }
+  static constexpr int KC = 32;
+  __device__ static f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) { return mfma16(a, b, c); }
 };
 
-// LDS row stride in elements: 16 bytes of padding keep rows 16-byte aligned
-// and move each row 4 banks on
+// Operands of global row `row` (W wide) for lane (n, g): step c holds
+// elements [c KC + g KC / 4, + KC / 4). Rows at or past n_rows read 0.
 template <typename T, int W>
-constexpr int lds_stride() {
-  return W + 16 / (int)sizeof(T);
-}
-
-// Operands of `row` (W wide, in global memory) for a lane's n index: step c
-// holds elements [c KC + h KC / 2, + KC / 2). Rows at or past n_rows read 0.
-template <typename T, int W>
-__device__ inline void load_row_ops(typename Wt<T>::op (&r)[W / Wt<T>::KC], const T* g, int row,
-                                    int n_rows, int hh) {
-  constexpr int KC = Wt<T>::KC;
+__device__ inline void load_row_ops(typename W16<T>::op (&r)[W / W16<T>::KC], const T* base, int row,
+                                    int n_rows, int g) {
+  constexpr int KC = W16<T>::KC;
   const bool ok = row < n_rows;
 #pragma unroll
   for (int c = 0; c < W / KC; ++c) {
     if constexpr (std::is_same<T, float>::value) {
-      r[c] = ok ? g[(long long)row * W + KC * c + hh] : 0.f;
+      r[c] = ok ? base[(long long)row * W + KC * c + g] : 0.f;
     } else {
-      r[c] = ok ? *reinterpret_cast<const bf16x8*>(g + (long long)row * W + KC * c + 8 * hh) : bf16x8{};
+      r[c] = ok ? *reinterpret_cast<const bf16x8*>(base + (long long)row * W + KC * c + 8 * g) : bf16x8{};
     }
   }
 }
 
-// The row operand of LDS row `row` at step c.
+// The same operand step of LDS tile row `row` (row stride rsb bytes).
 template <typename T>
-__device__ inline typename Wt<T>::op row_op(const FM_LDS T* t, int rs, int row, int c, int hh) {
+__device__ inline typename W16<T>::op row_op(const FM_LDS char* t, int rsb, int row, int c, int g) {
   if constexpr (std::is_same<T, float>::value) {
-    return t[row * rs + 2 * c + hh];
+    return *reinterpret_cast<const FM_LDS float*>(t + row * rsb + (4 * c + g) * 4);
   } else {
-    return *reinterpret_cast<const FM_LDS bf16x8*>(t + row * rs + 16 * c + 8 * hh);
+    return *reinterpret_cast<const FM_LDS bf16x8*>(t + row * rsb + (32 * c + 8 * g) * 2);
   }
 }
 
-// Column n of LDS rows [r0, r0 + 32) at step s of a contraction over those
-// rows in accumulator order.
-template <typename T>
-__device__ inline typename Wt<T>::op col_op(const FM_LDS T* t, int rs, int r0, int n, int s, int hh) {
-  if constexpr (std::is_same<T, float>::value) {
-    return t[(r0 + 8 * (s / 4) + 4 * hh + (s % 4)) * rs + n];
-  } else {
-    bf16x8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = t[(r0 + 16 * s + 8 * (e / 4) + 4 * hh + (e % 4)) * rs + n];
-    return v;
-  }
+// Column col0 + n of the 32 rows of an LDS tile as the operand of a
+// contraction over those rows, in score-accumulator order. bf16: the whole
+// contraction (32 rows) in one operand, from two transposed reads (each
+// 16-lane group reads a 4-row x 16-column block; lane n of group g receives
+// rows 4 g .. 4 g + 3, then 16 + 4 g .. 16 + 4 g + 3, of column col0 + n).
+// fp32: step s of 8, row 16 (s / 4) + 4 g + s % 4.
+__device__ inline bf16x8 col_tr(const FM_LDS char* t, int rsb, int col0, int lane) {
+  const int sl = lane & 15, g = lane >> 4;
+  const FM_LDS char* pa = t + (4 * g + (sl >> 2)) * rsb + (col0 + 4 * (sl & 3)) * 2;
+  return cat(lds_read_tr(pa), lds_read_tr(pa + 16 * rsb));
+}
+__device__ inline float col_f32(const FM_LDS char* t, int rsb, int col, int s, int g) {
+  return *reinterpret_cast<const FM_LDS float*>(t + (16 * (s / 4) + 4 * g + s % 4) * rsb + col * 4);
 }
 
-// Step s of an accumulator as the operand whose k runs over its M index
-// (bf16: rounded to nearest even).
+// Step s of the two score-shaped accumulators (rows 16 mt + 4 g + e) as the
+// operand of a contraction over their rows (bf16: all 32 rows, rounded to
+// nearest even).
 template <typename T>
-__device__ inline typename Wt<T>::op acc_op(const f32x16& a, int s) {
+__device__ inline typename W16<T>::op acc_op(const f32x4 (&a)[2], int s) {
   if constexpr (std::is_same<T, float>::value) {
-    return a[s];
+    return a[s / 4][s % 4];
   } else {
+    (void)s;
     bf16x8 v;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (bf16)a[8 * s + e];
+    for (int e = 0; e < 8; ++e) v[e] = (bf16)a[e / 4][e % 4];
     return v;
   }
 }
@@ -139,40 +141,28 @@ __device__ inline typename Wt<T>::op acc_op(const f32x16& a, int s) {
 // chain ahead of its first product and the registers run out.
 template <int N, int PF, typename Rd, typename Step>
 __device__ inline void chain(Rd rd, Step step) {
-  decltype(rd(0)) ring[PF];
+  constexpr int P = PF < N ? PF : N;
+  decltype(rd(0)) ring[P];
 #pragma unroll
-  for (int t = 0; t < PF; ++t) ring[t] = rd(t);
+  for (int t = 0; t < P; ++t) ring[t] = rd(t);
 #pragma unroll
   for (int t = 0; t < N; ++t) {
-    const auto a = ring[t % PF];
-    if (t + PF < N) ring[t % PF] = rd(t + PF);
+    const auto a = ring[t % P];
+    if (t + P < N) ring[t % P] = rd(t + P);
     step(t, a);
     __builtin_amdgcn_sched_barrier(0x406);
   }
 }
 
-// Rows [g0, g0 + R) of a row-major global matrix (row stride gw elements),
-// columns [col0, col0 + W), into LDS with row stride rs; rows at or past
-// n_rows as zeros. 16-byte pieces spread over the workgroup's 256 threads.
-template <typename T, int R, int W>
-__device__ inline void stage(FM_LDS T* t, int rs, const T* g, long long gw, int col0, int g0, int n_rows) {
-  constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int CPR = W / EPC;
-  for (int x = threadIdx.x; x < R * CPR; x += 256) {
-    const int row = x / CPR, c = x % CPR;
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (g0 + row < n_rows) v = *reinterpret_cast<const u32x4*>(g + (long long)(g0 + row) * gw + col0 + c * EPC);
-    *reinterpret_cast<FM_LDS u32x4*>(t + row * rs + c * EPC) = v;
-  }
+// max / sum over the four lanes of one accumulator column (n, n + 16,
+// n + 32, n + 48): a swap of 16-lane rows, then of 32-lane halves
+__device__ inline float max_x4(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_x32(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
-
-// Key bounds of keys [c0, c0 + 64) into vl ([4][64]: LTS, LTE, UTS, UTE),
-// absent vectors as 0 (the has_* flags gate their use).
-__device__ inline void stage_bounds(FM_LDS int* vl, const WideParams& p, long long vrow, int c0) {
-  const int vsel = threadIdx.x >> 6, kk = threadIdx.x & 63;
-  const int32_t* src = vsel == 0 ? p.lts : vsel == 1 ? p.lte : vsel == 2 ? p.uts : p.ute;
-  const bool present = src != nullptr && (vsel < 2 ? p.has_lt : p.has_ut);
-  vl[vsel * 64 + kk] = (present && c0 + kk < p.Nk) ? src[vrow + c0 + kk] : 0;
+__device__ inline float sum_x4(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return sum_x32(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
 // Whether the mask hides element (row i, key j), from key j's bounds.
@@ -188,412 +178,498 @@ __device__ inline bool hidden(const WideParams& p, int i, int j, int lts, int lt
   return m;
 }
 
-// -inf on the hidden elements of an S^T block (keys x rows) of a query-major
-// kernel: lane row i, key kbase + kl0 + M index; bounds from vl, read four
-// keys at a time before any test.
-__device__ inline void mask_st(f32x16& s, const FM_LDS int* vl, int kl0, int kbase, int i,
-                               const WideParams& p, int hh) {
-  f32x16 out;
+// Appends the visible tiles among [base, base + 256) of a workgroup's walk
+// to `list`, from position cnt: thread t tests tile base + t with cls(tile,
+// bits), which returns 0 for a tile the mask hides from the whole workgroup
+// and otherwise sets bits to the four waves' classes (2 bits each). An entry
+// is the tile index with the bits above bit 24. Returns the new count, the
+// same in every thread.
+template <typename Cls>
+__device__ inline int scan_chunk(FM_LDS int* list, FM_LDS int* wsum, int cnt, int base, int n, Cls cls) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t = base + tid;
+  unsigned bits = 0;
+  const bool valid = t < n && cls(t, bits) != 0;
+  const unsigned long long bal = __ballot(valid);
+  const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+  if (lane == 0) wsum[w] = __builtin_popcountll(bal);
+  __syncthreads();
+  int off = cnt, add = 0;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int kl = kl0 + 8 * g + 4 * hh;
-    const i32x4 lts4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 0 * 64 + kl);
-    const i32x4 lte4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 1 * 64 + kl);
-    const i32x4 uts4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 2 * 64 + kl);
-    const i32x4 ute4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 3 * 64 + kl);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool m = hidden(p, i, kbase + kl + e, lts4[e], lte4[e], uts4[e], ute4[e]);
-      out[4 * g + e] = m ? kNegInf : s[4 * g + e];
-    }
+  for (int ww = 0; ww < 4; ++ww) {
+    const int v = wsum[ww];
+    if (ww < w) off += v;
+    add += v;
   }
-  s = out;
+  if (valid) list[off + rank] = (int)((unsigned)t | (bits << 24));
+  __syncthreads();
+  return cnt + uniform(add);
 }
 
-// Query-major item order: chunk fastest (the chunks of one query block read
-// the same K tiles together), heavy (late) query blocks first.
-__device__ inline void qmajor_item(int nch, const WideParams& p, int& ch, int& bh, int& qb) {
-  const int t = (int)blockIdx.x;
-  ch = t % nch;
-  const int rest = t / nch;
-  const int BH = p.B * p.H;
-  bh = rest % BH;
-  qb = p.nqb - 1 - rest / BH;
+// Runs the tiles of `list` [0, cnt) through two LDS stages: tile it + 1
+// loads while tile it is computed. At step it only tile it's loads are in
+// flight; once every wave has them (the barrier) every wave is also done
+// with tile it - 1, whose stage then takes tile it + 1: one barrier per tile.
+template <typename Issue, typename Compute>
+__device__ inline void run_list(const FM_LDS int* list, int cnt, Issue issue, Compute compute) {
+  auto step = [&](int it, auto stage_c) {
+    const unsigned entry = uniform_u32((unsigned)list[it]);
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (it + 1 < cnt) issue(uniform_u32((unsigned)list[it + 1]), std::integral_constant<int, 1 - decltype(stage_c)::value>{});
+    compute(entry, stage_c);
+  };
+  if (cnt > 0) issue(uniform_u32((unsigned)list[0]), std::integral_constant<int, 0>{});
+  for (int it = 0; it < cnt; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < cnt) step(it + 1, std::integral_constant<int, 1>{});
+  }
+}
+
+// Rows [r0, r0 + 32) of a row-major head slice (resource r, CP 16-byte
+// pieces per row) into an LDS tile with row stride rsb bytes: wave w moves
+// rows w, w + 4, ..., one instruction per row. Rows past the slice read 0.
+template <int CP>
+__device__ inline void dma_rows(__amdgpu_buffer_rsrc_t r, FM_LDS char* dst, int rsb, int r0, int w, int lane) {
+  static_assert(CP <= 64, "one instruction per row");
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int row = w + 4 * k;
+    if (CP == 64 || lane < CP)
+      load_lds16(r, dst + row * rsb, (uint32_t)(r0 + row) * (uint32_t)(CP * 16) + 16u * (uint32_t)lane);
+  }
+}
+
+// A buffer resource over `n` int32 or float values at base (none when absent)
+template <typename V>
+__device__ inline __amdgpu_buffer_rsrc_t vec_rsrc(const V* base, long long off, int n, bool present) {
+  return make_rsrc(present ? base + off : nullptr, present ? (uint32_t)n * 4u : 0u);
 }
 
 // ---------------------------------------------------------------- forward
-// Workgroup: 128 query rows (32 per wave), output columns
-// [ch DVC, (ch + 1) DVC) of O. Per visible 64-key tile: S^T = K Q^T (Q in
+// Workgroup: 64 query rows (16 per wave) and every output column. Per visible
+// 32-key tile (K, V and the keys' bounds in LDS): S^T = K Q^T (Q in
 // registers), the tile's mask, online softmax, O^T += V^T P^T.
-template <typename T, int D, int DV, int DVC>
-__global__ __launch_bounds__(256, 1) void wide_fwd_kernel(WideParams p) {
-  using X = Wt<T>;
-  constexpr int BC = 64, BR = 128, NCH = DV / DVC, KC = X::KC;
-  constexpr int KS = lds_stride<T, D>(), VS = lds_stride<T, DVC>();
-  __shared__ __attribute__((aligned(16))) T ks_[BC * KS];
-  __shared__ __attribute__((aligned(16))) T vs_[BC * VS];
-  __shared__ int vl_[4 * 64];
-  FM_LDS T* ks = (FM_LDS T*)ks_;
-  FM_LDS T* vs = (FM_LDS T*)vs_;
-  FM_LDS int* vl = (FM_LDS int*)vl_;
+template <typename T, int D, int DV>
+struct WFwd {
+  static constexpr int BR = 64, BC = 32;
+  static constexpr int RSK = D * (int)sizeof(T) + 16;    // LDS row strides (bytes): K is read by rows,
+  static constexpr int RSV = DV * (int)sizeof(T) + 32;   // V by transposed 4-row blocks
+  static constexpr int CPK = D * (int)sizeof(T) / 16, CPV = DV * (int)sizeof(T) / 16;
+  static constexpr int KT = BC * RSK, VT = BC * RSV;
+  static constexpr int STAGE = KT + VT + 4 * BC * 4;     // K, V, LTS/LTE/UTS/UTE of the keys
+  static constexpr int LIST = 512;
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = uniform(tid >> 6);
-  const int hh = lane >> 5;
-  const int l32 = lane & 31;
-  int ch, bh, qb;
-  qmajor_item(NCH, p, ch, bh, qb);
-  const int b = bh / p.H, h = bh % p.H;
-  const int hmi = p.hm == 1 ? 0 : h;
-  const int Nq = p.Nq, Nk = p.Nk;
-  const bool causal = p.causal != 0;
-  const long long qslice = (long long)bh * Nq, kslice = (long long)bh * Nk;
-  const int r0 = qb * BR, r1 = min(Nq, r0 + BR);
-  const int i = r0 + 32 * w + l32;
-  const T* kg = reinterpret_cast<const T*>(p.k) + kslice * D;
-  const T* vg = reinterpret_cast<const T*>(p.v) + kslice * DV;
-  const long long vrow = ((long long)b * p.hm + hmi) * Nk;
-  const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb64 * 8;
-
-  typename X::op qf[D / KC];
-  load_row_ops<T, D>(qf, reinterpret_cast<const T*>(p.q) + qslice * D, i, Nq, hh);
-  f32x16 oacc[DVC / 32];
+// -inf on the hidden elements of two S^T blocks (lane: row i; keys
+// kbase + 16 jb + 4 g + e) from the keys' bounds in vl ([4][32]), read four
+// keys at a time before any test.
+__device__ inline void mask_rows(f32x4 (&s)[2], const FM_LDS int* vl, int kbase, int i, const WideParams& p, int g) {
 #pragma unroll
-  for (int mb = 0; mb < DVC / 32; ++mb) oacc[mb] = f32x16{};
-  float m_run = kNegInf, l_run = 0.f;
-  unsigned cnt0 = 0, cnt1 = 0, cnt2 = 0;
-
-  for (int kb = 0; kb < p.nkb64; ++kb) {
-    const BlockBounds bb = load_bounds(table + (long long)kb * 8);
-    const int c0 = kb * BC, c1 = min(Nk, c0 + BC);
-    const int wgc = tile_class(bb, r0, r1, c0, c1, causal);
-    cnt0 += wgc == 0;
-    cnt1 += wgc == 1;
-    cnt2 += wgc == 2;
-    if (wgc == 0) continue;
-    int wc = 0;
-    const int a0 = r0 + 32 * w;
-    if (a0 < Nq) {
-      wc = tile_class(bb, a0, min(Nq, a0 + 32), c0, c1, causal);
-      if (c1 - c0 < BC && wc == 2) wc = 1;
+  for (int jb = 0; jb < 2; ++jb) {
+    const int kl = 16 * jb + 4 * g;
+    const i32x4 lts4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 0 * 32 + kl);
+    const i32x4 lte4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 1 * 32 + kl);
+    const i32x4 uts4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 2 * 32 + kl);
+    const i32x4 ute4 = *reinterpret_cast<const FM_LDS i32x4*>(vl + 3 * 32 + kl);
+    f32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool m = hidden(p, i, kbase + kl + e, lts4[e], lte4[e], uts4[e], ute4[e]);
+      out[e] = m ? kNegInf : s[jb][e];
     }
-    __syncthreads();   // the last tile's readers are done
-    stage<T, BC, D>(ks, KS, kg, D, 0, c0, Nk);
-    stage<T, BC, DVC>(vs, VS, vg, DV, ch * DVC, c0, Nk);
-    stage_bounds(vl, p, vrow, c0);
-    __syncthreads();
-    if (wc == 0) continue;
-    f32x16 s[2];
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      s[jb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < D / KC; ++c) s[jb] = X::mma(row_op<T>(ks, KS, jb * 32 + l32, c, hh), qf[c], s[jb]);
-      if (wc == 1) mask_st(s[jb], vl, jb * 32, c0, i, p, hh);
-    }
-    // online softmax, base 2; a row with nothing open keeps offset -inf
-    const float mx = max_x32(max_acc(s));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2f((m_run - m_use) * p.sl2);
-    const float msl = m_use * p.sl2;
-    float rs = 0.f;
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = exp2f(__builtin_fmaf(s[jb][r], p.sl2, -msl));
-        // bf16: the row sum takes the rounded values the PV product uses
-        if constexpr (!std::is_same<T, float>::value) pv = (float)(bf16)pv;
-        s[jb][r] = pv;
-        rs += pv;
-      }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int mb = 0; mb < DVC / 32; ++mb) oacc[mb] *= alpha;
-    // O^T += V^T P^T over the tile's 64 keys
-#pragma unroll
-    for (int mb = 0; mb < DVC / 32; ++mb)
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int st = 0; st < 32 / KC; ++st)
-          oacc[mb] = X::mma(col_op<T>(vs, VS, jb * 32, 32 * mb + l32, st, hh), acc_op<T>(s[jb], st), oacc[mb]);
-  }
-
-  const float lt = sum_x32(l_run);
-  float inv, row_lse;
-  finish_row(lt, m_run, p.scale, p.sink != nullptr ? p.sink[h] : kNegInf, p.sink != nullptr, inv, row_lse);
-  if (i < Nq) {
-    T* og = reinterpret_cast<T*>(p.o) + (qslice + i) * DV + ch * DVC;
-#pragma unroll
-    for (int mb = 0; mb < DVC / 32; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // this lane's columns 32 mb + 8 g + 4 h + e, e < 4
-        if constexpr (std::is_same<T, float>::value) {
-          f32x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = oacc[mb][4 * g + e] * inv;
-          *reinterpret_cast<f32x4*>(og + 32 * mb + 8 * g + 4 * hh) = v4;
-        } else {
-          bf16x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[mb][4 * g + e] * inv);
-          *reinterpret_cast<bf16x4*>(og + 32 * mb + 8 * g + 4 * hh) = v4;
-        }
-      }
-    if (ch == 0 && hh == 0) p.lse[qslice + i] = row_lse;
-  }
-  if (ch == 0 && p.counts != nullptr && tid == 0) {
-    atomicAdd(p.counts + 0, (unsigned long long)cnt0);
-    atomicAdd(p.counts + 1, (unsigned long long)cnt1);
-    atomicAdd(p.counts + 2, (unsigned long long)cnt2);
+    s[jb] = out;
   }
 }
 
-// ---------------------------------------------------------------- dQ pass
-// Workgroup: 128 query rows, dQ columns [ch DC, (ch + 1) DC). Q and dO rows
-// in registers; per visible 64-key tile (K and V in LDS):
-//   S^T = K Q^T, dP^T = V dO^T, the tile's mask,
-//   P = exp2(S scale log2e - LSE2), dS = P (dP - delta),
-//   dQ^T += K^T dS^T (this chunk's columns of K).
-// delta and LSE2 come from the preprocess. dQ sums over the keys in a fixed
-// order in registers and is written once.
-template <typename T, int D, int DV, int DC>
-__global__ __launch_bounds__(256, 1) void wide_dq_kernel(WideParams p) {
-  using X = Wt<T>;
-  constexpr int BC = 64, BR = 128, NCH = D / DC, KC = X::KC;
-  constexpr int KS = lds_stride<T, D>(), VS = lds_stride<T, DV>();
-  __shared__ __attribute__((aligned(16))) T ks_[BC * KS];
-  __shared__ __attribute__((aligned(16))) T vs_[BC * VS];
-  __shared__ int vl_[4 * 64];
-  FM_LDS T* ks = (FM_LDS T*)ks_;
-  FM_LDS T* vs = (FM_LDS T*)vs_;
-  FM_LDS int* vl = (FM_LDS int*)vl_;
+// Classes of 32-key tile t for a query-major workgroup (rows [r0, r1), waves
+// of 16 rows from r0) from its 64-key table entry; the tile counters take
+// the entry's own class once (even t), at the reported 64 x 64 tile shape.
+__device__ inline int qmajor_class(const int32_t* table, const WideParams& p, int r0, int r1, int t,
+                                   unsigned& bits, unsigned (&cnt)[3]) {
+  const BlockBounds bb = load_bounds(table + (long long)(t >> 1) * 8);
+  const bool causal = p.causal != 0;
+  const int c0 = 32 * t, c1 = min(p.Nk, c0 + 32);
+  if ((t & 1) == 0) {
+    const int e = tile_class(bb, r0, r1, c0, min(p.Nk, c0 + 64), causal);
+    cnt[0] += e == 0;
+    cnt[1] += e == 1;
+    cnt[2] += e == 2;
+  }
+  const int wgc = tile_class(bb, r0, r1, c0, c1, causal);
+  if (wgc == 0) return 0;
+  const bool ragged = c1 - c0 < 32;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    const int a0 = r0 + 16 * ww;
+    int cl = 0;
+    if (a0 < p.Nq) {
+      cl = tile_class(bb, a0, min(p.Nq, a0 + 16), c0, c1, causal);
+      if (ragged && cl == 2) cl = 1;
+    }
+    bits |= (unsigned)cl << (2 * ww);
+  }
+  return wgc;
+}
+
+// Adds per-thread tile counts into the call's counters (once per workgroup).
+__device__ inline void flush_counts(unsigned long long* counts, unsigned* wcount, const unsigned (&cnt)[3]) {
+  if (counts == nullptr) return;
+  atomicAdd(&wcount[0], cnt[0]);
+  atomicAdd(&wcount[1], cnt[1]);
+  atomicAdd(&wcount[2], cnt[2]);
+  __syncthreads();
+  if (threadIdx.x < 3) atomicAdd(counts + threadIdx.x, (unsigned long long)wcount[threadIdx.x]);
+}
+
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(256, 1) void wide_fwd_kernel(WideParams p) {
+  using X = W16<T>;
+  using C = WFwd<T, D, DV>;
+  constexpr int KC = X::KC, PF = 6;
+  __shared__ __attribute__((aligned(16))) char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1[C::STAGE];
+  __shared__ int list_[C::LIST];
+  __shared__ int wsum_[4];
+  __shared__ unsigned wcount_[3];
+  FM_LDS int* list = (FM_LDS int*)list_;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = uniform(tid >> 6);
-  const int hh = lane >> 5;
-  const int l32 = lane & 31;
-  int ch, bh, qb;
-  qmajor_item(NCH, p, ch, bh, qb);
+  const int g = lane >> 4, n16 = lane & 15;
+  int bh, blk;
+  xcd_order((int)blockIdx.x, p.B * p.H, p.nqb, bh, blk);   // a head's blocks on one XCD
+  const int qb = p.nqb - 1 - blk;                           // heavy (late) blocks first
   const int b = bh / p.H, h = bh % p.H;
   const int hmi = p.hm == 1 ? 0 : h;
   const int Nq = p.Nq, Nk = p.Nk;
-  const bool causal = p.causal != 0;
   const long long qslice = (long long)bh * Nq, kslice = (long long)bh * Nk;
-  const int r0 = qb * BR, r1 = min(Nq, r0 + BR);
-  const int i = r0 + 32 * w + l32;
-  const T* kg = reinterpret_cast<const T*>(p.k) + kslice * D;
-  const T* vg = reinterpret_cast<const T*>(p.v) + kslice * DV;
+  const int r0 = qb * C::BR, r1 = min(Nq, r0 + C::BR);
+  const int i = r0 + 16 * w + n16;   // this lane's row
+  if (tid < 3) wcount_[tid] = 0;
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(uniform_ptr(reinterpret_cast<const T*>(p.k) + kslice * D), (uint32_t)Nk * (uint32_t)(C::CPK * 16));
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(uniform_ptr(reinterpret_cast<const T*>(p.v) + kslice * DV), (uint32_t)Nk * (uint32_t)(C::CPV * 16));
   const long long vrow = ((long long)b * p.hm + hmi) * Nk;
+  // bound vector w for wave w's share of each tile's loads
+  const __amdgpu_buffer_rsrc_t rb = w == 0   ? vec_rsrc(p.lts, vrow, Nk, p.has_lt != 0)
+                                    : w == 1 ? vec_rsrc(p.lte, vrow, Nk, p.has_lte != 0)
+                                    : w == 2 ? vec_rsrc(p.uts, vrow, Nk, p.has_ut != 0)
+                                             : vec_rsrc(p.ute, vrow, Nk, p.has_ut != 0);
   const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb64 * 8;
 
-  typename X::op qf[D / KC], dof[DV / KC];
-  load_row_ops<T, D>(qf, reinterpret_cast<const T*>(p.q) + qslice * D, i, Nq, hh);
-  load_row_ops<T, DV>(dof, reinterpret_cast<const T*>(p.dout) + qslice * DV, i, Nq, hh);
-  // a row past Nq gets LSE2 = +inf, so its P (and dQ, not stored) is 0
-  const float lse2 = i < Nq ? p.lse2[qslice + i] : __builtin_inff();
-  const float delta = i < Nq ? p.delta[qslice + i] : 0.f;
-  f32x16 dq[DC / 32];
+  typename X::op qf[D / KC];
+  load_row_ops<T, D>(qf, reinterpret_cast<const T*>(p.q) + qslice * D, i, Nq, g);
+  f32x4 oacc[DV / 16];
 #pragma unroll
-  for (int mb = 0; mb < DC / 32; ++mb) dq[mb] = f32x16{};
-  float pd = 0.f;   // this lane's part of rowsum(dS)
+  for (int mb = 0; mb < DV / 16; ++mb) oacc[mb] = f32x4{};
+  float m_run = kNegInf, l_run = 0.f;
+  unsigned cnt3[3] = {0u, 0u, 0u};
 
-  for (int kb = 0; kb < p.nkb64; ++kb) {
-    const BlockBounds bb = load_bounds(table + (long long)kb * 8);
-    const int c0 = kb * BC, c1 = min(Nk, c0 + BC);
-    if (tile_class(bb, r0, r1, c0, c1, causal) == 0) continue;
-    int wc = 0;
-    const int a0 = r0 + 32 * w;
-    if (a0 < Nq) {
-      wc = tile_class(bb, a0, min(Nq, a0 + 32), c0, c1, causal);
-      if (c1 - c0 < BC && wc == 2) wc = 1;
+  auto issue = [&](unsigned entry, auto stage_c) {
+    FM_LDS char* st = (FM_LDS char*)(decltype(stage_c)::value ? stage1 : stage0);
+    const int c0 = (int)(entry & 0xFFFFFFu) * C::BC;
+    dma_rows<C::CPK>(rk, st, C::RSK, c0, w, lane);
+    dma_rows<C::CPV>(rv, st + C::KT, C::RSV, c0, w, lane);
+    if (lane < 8) load_lds16(rb, st + C::KT + C::VT + w * C::BC * 4, (uint32_t)(c0 + 4 * lane) * 4u);
+  };
+
+  auto compute = [&](unsigned entry, auto stage_c) {
+    const int wc = (int)((entry >> (24 + 2 * w)) & 3u);
+    if (wc == 0) return;
+    const FM_LDS char* kst = (const FM_LDS char*)(decltype(stage_c)::value ? stage1 : stage0);
+    const FM_LDS char* vst = kst + C::KT;
+    const FM_LDS int* vl = (const FM_LDS int*)(kst + C::KT + C::VT);
+    const int c0 = (int)(entry & 0xFFFFFFu) * C::BC;
+    // S^T for the tile's two 16-key blocks, the two chains alternating
+    f32x4 s[2] = {f32x4{}, f32x4{}};
+    chain<2 * (D / KC), PF>([&](int t) { return row_op<T>(kst, C::RSK, 16 * (t & 1) + n16, t >> 1, g); },
+                            [&](int t, typename X::op a) { s[t & 1] = X::mma(a, qf[t >> 1], s[t & 1]); });
+    if (wc == 1) mask_rows(s, vl, c0, i, p, g);
+    // online softmax, base 2: the offset (and O and the row sum with it)
+    // moves only when some row's maximum outgrew it by more than the slack;
+    // a row with nothing open keeps offset -inf
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = max_x4(mx);
+    if (__ballot((mx - m_run) * p.sl2 > 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == kNegInf ? 1.f : fast_exp2((m_run - m_new) * p.sl2);
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < DV / 16; ++mb) oacc[mb] *= alpha;
+      m_run = m_new;
     }
-    __syncthreads();
-    stage<T, BC, D>(ks, KS, kg, D, 0, c0, Nk);
-    stage<T, BC, DV>(vs, VS, vg, DV, 0, c0, Nk);
-    stage_bounds(vl, p, vrow, c0);
-    __syncthreads();
-    if (wc == 0) continue;
+    const float msl = (m_run == kNegInf ? 0.f : m_run) * p.sl2;
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-      for (int c = 0; c < D / KC; ++c) s = X::mma(row_op<T>(ks, KS, jb * 32 + l32, c, hh), qf[c], s);
-#pragma unroll
-      for (int c = 0; c < DV / KC; ++c) dp = X::mma(row_op<T>(vs, VS, jb * 32 + l32, c, hh), dof[c], dp);
-      if (wc == 1) mask_st(s, vl, jb * 32, c0, i, p, hh);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float ds = exp2f(__builtin_fmaf(s[r], p.sl2, -lse2)) * (dp[r] - delta);
-        pd += ds;
-        s[r] = ds;
+      for (int e = 0; e < 4; ++e) {
+        float pv = fast_exp2(__builtin_fmaf(s[jb][e], p.sl2, -msl));
+        // bf16: the row sum takes the rounded values the PV product uses
+        if constexpr (!std::is_same<T, float>::value) pv = (float)(bf16)pv;
+        s[jb][e] = pv;
+        l_run += pv;
       }
-#pragma unroll
-      for (int mb = 0; mb < DC / 32; ++mb)
-#pragma unroll
-        for (int st = 0; st < 32 / KC; ++st)
-          dq[mb] = X::mma(col_op<T>(ks, KS, jb * 32, ch * DC + 32 * mb + l32, st, hh), acc_op<T>(s, st), dq[mb]);
+    // O^T += V^T P^T over the tile's 32 keys
+    if constexpr (std::is_same<T, float>::value) {
+      constexpr int NB = DV / 16;
+      chain<NB * 8, PF>([&](int t) { return col_f32(vst, C::RSV, 16 * (t % NB) + n16, t / NB, g); },
+                        [&](int t, float a) { oacc[t % NB] = X::mma(a, acc_op<T>(s, t / NB), oacc[t % NB]); });
+    } else {
+      const bf16x8 pop = acc_op<T>(s, 0);
+      chain<DV / 16, PF>([&](int t) { return col_tr(vst, C::RSV, 16 * t, lane); },
+                         [&](int t, bf16x8 a) { oacc[t] = X::mma(a, pop, oacc[t]); });
+    }
+  };
+
+  const int nkt = (Nk + C::BC - 1) / C::BC;
+  int cnt = 0;
+  for (int base = 0; base < nkt; base += 256) {
+    cnt = scan_chunk(list, (FM_LDS int*)wsum_, cnt, base, nkt,
+                     [&](int t, unsigned& bits) { return qmajor_class(table, p, r0, r1, t, bits, cnt3); });
+    if (cnt > C::LIST - 256 || base + 256 >= nkt) {
+      run_list(list, cnt, issue, compute);
+      cnt = 0;
     }
   }
 
-  pd = sum_x32(pd);
-  if (ch == 0 && p.pdsum != nullptr && i < Nq && hh == 0) p.pdsum[qslice + i] = pd;
+  const float lt = sum_x4(l_run);
+  float inv, row_lse;
+  finish_row(lt, m_run, p.scale, p.sink != nullptr ? p.sink[h] : kNegInf, p.sink != nullptr, inv, row_lse);
   if (i < Nq) {
-    T* dqg = reinterpret_cast<T*>(p.dq) + (qslice + i) * D + ch * DC;
+    // lane: row i, columns 16 mb + 4 g + e
+    T* og = reinterpret_cast<T*>(p.o) + (qslice + i) * DV + 4 * g;
 #pragma unroll
-    for (int mb = 0; mb < DC / 32; ++mb)
+    for (int mb = 0; mb < DV / 16; ++mb) {
+      if constexpr (std::is_same<T, float>::value) {
+        *reinterpret_cast<f32x4*>(og + 16 * mb) = oacc[mb] * inv;
+      } else {
+        bf16x4 v4;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if constexpr (std::is_same<T, float>::value) {
-          f32x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = dq[mb][4 * g + e] * p.scale;
-          *reinterpret_cast<f32x4*>(dqg + 32 * mb + 8 * g + 4 * hh) = v4;
-        } else {
-          bf16x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(dq[mb][4 * g + e] * p.scale);
-          *reinterpret_cast<bf16x4*>(dqg + 32 * mb + 8 * g + 4 * hh) = v4;
-        }
+        for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[mb][e] * inv);
+        *reinterpret_cast<bf16x4*>(og + 16 * mb) = v4;
       }
+    }
+    if (g == 0) p.lse[qslice + i] = row_lse;
+  }
+  flush_counts(p.counts, wcount_, cnt3);
+}
+
+// ---------------------------------------------------------------- dQ pass
+// Workgroup: 64 query rows, every dQ column. Q and dO rows in registers;
+// per visible 32-key tile (K and V in LDS):
+//   S^T = K Q^T, dP^T = V dO^T, the tile's mask,
+//   P = exp2(S scale log2e - LSE2), dS = P (dP - delta),
+//   dQ^T += K^T dS^T.
+// delta and LSE2 come from the preprocess. dQ sums over the keys in a fixed
+// order in registers and is written once.
+template <typename T, int D, int DV>
+struct WDq {
+  static constexpr int BR = 64, BC = 32;
+  static constexpr int RSK = D * (int)sizeof(T) + 16;    // K: by rows and transposed
+  static constexpr int RSV = DV * (int)sizeof(T) + 16;   // V: by rows
+  static constexpr int CPK = D * (int)sizeof(T) / 16, CPV = DV * (int)sizeof(T) / 16;
+  static constexpr int KT = BC * RSK, VT = BC * RSV;
+  static constexpr int STAGE = KT + VT + 4 * BC * 4;
+  static constexpr int LIST = 512;
+};
+
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(256, 1) void wide_dq_kernel(WideParams p) {
+  using X = W16<T>;
+  using C = WDq<T, D, DV>;
+  constexpr int KC = X::KC, PF = 6;
+  __shared__ __attribute__((aligned(16))) char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1[C::STAGE];
+  __shared__ int list_[C::LIST];
+  __shared__ int wsum_[4];
+  FM_LDS int* list = (FM_LDS int*)list_;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int g = lane >> 4, n16 = lane & 15;
+  int bh, blk;
+  xcd_order((int)blockIdx.x, p.B * p.H, p.nqb, bh, blk);
+  const int qb = p.nqb - 1 - blk;
+  const int b = bh / p.H, h = bh % p.H;
+  const int hmi = p.hm == 1 ? 0 : h;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const long long qslice = (long long)bh * Nq, kslice = (long long)bh * Nk;
+  const int r0 = qb * C::BR, r1 = min(Nq, r0 + C::BR);
+  const int i = r0 + 16 * w + n16;
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(uniform_ptr(reinterpret_cast<const T*>(p.k) + kslice * D), (uint32_t)Nk * (uint32_t)(C::CPK * 16));
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(uniform_ptr(reinterpret_cast<const T*>(p.v) + kslice * DV), (uint32_t)Nk * (uint32_t)(C::CPV * 16));
+  const long long vrow = ((long long)b * p.hm + hmi) * Nk;
+  const __amdgpu_buffer_rsrc_t rb = w == 0   ? vec_rsrc(p.lts, vrow, Nk, p.has_lt != 0)
+                                    : w == 1 ? vec_rsrc(p.lte, vrow, Nk, p.has_lte != 0)
+                                    : w == 2 ? vec_rsrc(p.uts, vrow, Nk, p.has_ut != 0)
+                                             : vec_rsrc(p.ute, vrow, Nk, p.has_ut != 0);
+  const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb64 * 8;
+
+  typename X::op qf[D / KC], dof[DV / KC];
+  load_row_ops<T, D>(qf, reinterpret_cast<const T*>(p.q) + qslice * D, i, Nq, g);
+  load_row_ops<T, DV>(dof, reinterpret_cast<const T*>(p.dout) + qslice * DV, i, Nq, g);
+  // a row past Nq gets LSE2 = +inf, so its P (and dQ, not stored) is 0
+  const float lse2 = i < Nq ? p.lse2[qslice + i] : __builtin_inff();
+  const float delta = i < Nq ? p.delta[qslice + i] : 0.f;
+  f32x4 dq[D / 16];
+#pragma unroll
+  for (int mb = 0; mb < D / 16; ++mb) dq[mb] = f32x4{};
+  float pd = 0.f;   // this lane's part of rowsum(dS)
+  unsigned cnt3[3] = {0u, 0u, 0u};   // (the dK/dV pass reports the tiles)
+
+  auto issue = [&](unsigned entry, auto stage_c) {
+    FM_LDS char* st = (FM_LDS char*)(decltype(stage_c)::value ? stage1 : stage0);
+    const int c0 = (int)(entry & 0xFFFFFFu) * C::BC;
+    dma_rows<C::CPK>(rk, st, C::RSK, c0, w, lane);
+    dma_rows<C::CPV>(rv, st + C::KT, C::RSV, c0, w, lane);
+    if (lane < 8) load_lds16(rb, st + C::KT + C::VT + w * C::BC * 4, (uint32_t)(c0 + 4 * lane) * 4u);
+  };
+
+  auto compute = [&](unsigned entry, auto stage_c) {
+    const int wc = (int)((entry >> (24 + 2 * w)) & 3u);
+    if (wc == 0) return;
+    const FM_LDS char* kst = (const FM_LDS char*)(decltype(stage_c)::value ? stage1 : stage0);
+    const FM_LDS char* vst = kst + C::KT;
+    const FM_LDS int* vl = (const FM_LDS int*)(kst + C::KT + C::VT);
+    const int c0 = (int)(entry & 0xFFFFFFu) * C::BC;
+    // S^T and dP^T for the tile's two 16-key blocks: step u of a product is
+    // block u & 1, operand step u >> 1; the two products alternate while
+    // both have steps left
+    constexpr int NS = 2 * (D / KC), ND = 2 * (DV / KC), NMIN = NS < ND ? NS : ND;
+    auto is_dp = [](int t) { return t < 2 * NMIN ? (t & 1) != 0 : ND > NS; };
+    auto ustep = [](int t) { return t < 2 * NMIN ? t >> 1 : t - NMIN; };
+    f32x4 s[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
+    chain<NS + ND, PF>(
+        [&](int t) {
+          const int u = ustep(t);
+          return is_dp(t) ? row_op<T>(vst, C::RSV, 16 * (u & 1) + n16, u >> 1, g)
+                          : row_op<T>(kst, C::RSK, 16 * (u & 1) + n16, u >> 1, g);
+        },
+        [&](int t, typename X::op a) {
+          const int u = ustep(t);
+          if (is_dp(t)) dp[u & 1] = X::mma(a, dof[u >> 1], dp[u & 1]);
+          else s[u & 1] = X::mma(a, qf[u >> 1], s[u & 1]);
+        });
+    if (wc == 1) mask_rows(s, vl, c0, i, p, g);
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ds = fast_exp2(__builtin_fmaf(s[jb][e], p.sl2, -lse2)) * (dp[jb][e] - delta);
+        pd += ds;
+        s[jb][e] = ds;
+      }
+    // dQ^T += K^T dS^T over the tile's 32 keys (dQ takes the scale at the end)
+    if constexpr (std::is_same<T, float>::value) {
+      constexpr int NB = D / 16;
+      chain<NB * 8, PF>([&](int t) { return col_f32(kst, C::RSK, 16 * (t % NB) + n16, t / NB, g); },
+                        [&](int t, float a) { dq[t % NB] = X::mma(a, acc_op<T>(s, t / NB), dq[t % NB]); });
+    } else {
+      const bf16x8 dsop = acc_op<T>(s, 0);
+      chain<D / 16, PF>([&](int t) { return col_tr(kst, C::RSK, 16 * t, lane); },
+                        [&](int t, bf16x8 a) { dq[t] = X::mma(a, dsop, dq[t]); });
+    }
+  };
+
+  const int nkt = (Nk + C::BC - 1) / C::BC;
+  int cnt = 0;
+  for (int base = 0; base < nkt; base += 256) {
+    cnt = scan_chunk(list, (FM_LDS int*)wsum_, cnt, base, nkt,
+                     [&](int t, unsigned& bits) { return qmajor_class(table, p, r0, r1, t, bits, cnt3); });
+    if (cnt > C::LIST - 256 || base + 256 >= nkt) {
+      run_list(list, cnt, issue, compute);
+      cnt = 0;
+    }
+  }
+
+  pd = sum_x4(pd);
+  if (p.pdsum != nullptr && i < Nq && g == 0) p.pdsum[qslice + i] = pd;
+  if (i < Nq) {
+    T* dqg = reinterpret_cast<T*>(p.dq) + (qslice + i) * D + 4 * g;
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) {
+      if constexpr (std::is_same<T, float>::value) {
+        *reinterpret_cast<f32x4*>(dqg + 16 * mb) = dq[mb] * p.scale;
+      } else {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (bf16)(dq[mb][e] * p.scale);
+        *reinterpret_cast<bf16x4*>(dqg + 16 * mb) = v4;
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------- dK/dV pass
-// 16x16 MFMAs (v_mfma_f32_16x16x32_bf16, v_mfma_f32_16x16x4_f32): lane
-// (n = lane % 16, k-group g = lane / 16) operands, and a 16x16 accumulator
-// in which lane (n, g) holds M index 4 g + e in register e. With 16 keys per
-// wave a lane keeps a quarter of its key's K and V rows (64 registers each
-// at these widths) where the 32x32 shape would need all 256 architectural
-// VGPRs for the two rows.
-template <typename T>
-struct W16;
-template <>
-struct W16<float> {
-  using op = float;
-  static constexpr int KC = 4;
-  __device__ static f32x4 mma(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-  }
-};
-template <>
-struct W16<bf16> {
-  using op = bf16x8;
-  static constexpr int KC = 32;
-  __device__ static f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) { return mfma16(a, b, c); }
-};
-
-// Operand step c of a row (k along the row): elements [c KC + g KC / 4, + KC / 4)
-template <typename T>
-__device__ inline typename W16<T>::op row_op16(const FM_LDS T* t, int rs, int row, int c, int g) {
-  if constexpr (std::is_same<T, float>::value) {
-    return t[row * rs + 4 * c + g];
-  } else {
-    return *reinterpret_cast<const FM_LDS bf16x8*>(t + row * rs + 32 * c + 8 * g);
-  }
-}
-
-// The 32 rows of a query step in the order of the S accumulators: operand
-// step s, k-group g, element e is row 16 (e / 4) + 4 g + e % 4 (bf16, one
-// step) or row 16 (s / 4) + 4 g + s % 4 (fp32, eight steps).
-template <typename T>
-__device__ inline typename W16<T>::op col_op16(const FM_LDS T* t, int rs, int n, int s, int g) {
-  if constexpr (std::is_same<T, float>::value) {
-    return t[(16 * (s / 4) + 4 * g + (s % 4)) * rs + n];
-  } else {
-    bf16x8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = t[(16 * (e / 4) + 4 * g + (e % 4)) * rs + n];
-    return v;
-  }
-}
-
-// The same step of the two S-shaped accumulators (rows 16 mt + 4 g + e).
-template <typename T>
-__device__ inline typename W16<T>::op acc_op16(const f32x4 (&a)[2], int s) {
-  if constexpr (std::is_same<T, float>::value) {
-    return a[s / 4][s % 4];
-  } else {
-    bf16x8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (bf16)a[e / 4][e % 4];
-    return v;
-  }
-}
-
 // Workgroup: 64 keys (16 per wave), chunk ch of NCH: dK columns
 // [ch KCK, (ch + 1) KCK) and dV columns [ch KCV, (ch + 1) KCV), KCK = D / NCH,
-// KCV = DV / NCH.
-// K and V rows of the lane's key in registers; per visible 32-row query
-// step (Q, dO, LSE2 and delta in LDS):
+// KCV = DV / NCH. K and V rows of the lane's key in registers; per visible
+// 32-row query step (Q, dO, LSE2 and delta in LDS):
 //   S = Q K^T, dP = dO V^T, the mask from the key's own bounds,
 //   P = exp2(S scale log2e - LSE2), dS = P (dP - delta),
 //   dV^T += dO^T P and dK^T += Q^T dS (this chunk's columns; dK takes the
 //   scale once, at the end).
+template <typename T, int D, int DV>
+struct WKv {
+  static constexpr int BKC = 64, BQ = 32;
+  static constexpr int RSQ = D * (int)sizeof(T) + 16;   // Q and dO: by rows and transposed
+  static constexpr int RSO = DV * (int)sizeof(T) + 16;
+  static constexpr int CPQ = D * (int)sizeof(T) / 16, CPO = DV * (int)sizeof(T) / 16;
+  static constexpr int QT = BQ * RSQ, OT = BQ * RSO;
+  static constexpr int STAGE = QT + OT + 2 * BQ * 4;   // Q, dO, LSE2, delta
+  static constexpr int LIST = 512;
+};
+
 template <typename T, int D, int DV, int NCH>
 __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
   using X = W16<T>;
+  using C = WKv<T, D, DV>;
   constexpr int KCK = D / NCH, KCV = DV / NCH;
   static_assert(KCK * NCH == D && KCV * NCH == DV && KCK % 16 == 0 && KCV % 16 == 0, "column chunks");
-  constexpr int KW = 16, BKC = 64, BQ = 32, KC = X::KC;
-  constexpr int QS = lds_stride<T, D>(), OS = lds_stride<T, DV>();
-  __shared__ __attribute__((aligned(16))) T qs_[BQ * QS];
-  __shared__ __attribute__((aligned(16))) T dos_[BQ * OS];
-  __shared__ float lse_s[BQ];
-  __shared__ float del_s[BQ];
-  FM_LDS T* qs = (FM_LDS T*)qs_;
-  FM_LDS T* dos = (FM_LDS T*)dos_;
+  constexpr int KC = X::KC, PF = 6;
+  __shared__ __attribute__((aligned(16))) char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1[C::STAGE];
+  __shared__ int list_[C::LIST];
+  __shared__ int wsum_[4];
+  __shared__ unsigned wcount_[3];
+  FM_LDS int* list = (FM_LDS int*)list_;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = uniform(tid >> 6);
-  const int g = lane >> 4;
-  const int n16 = lane & 15;
+  const int g = lane >> 4, n16 = lane & 15;
   const int BH = p.B * p.H;
   const int ch = (int)(blockIdx.x % NCH);
-  const int rest = (int)(blockIdx.x / NCH);
-  const int bh = rest % BH;
-  const int kb = rest / BH;
+  int bh, kb;
+  xcd_order((int)(blockIdx.x / NCH), BH, p.nkb64, bh, kb);   // early (heavy) key blocks first
   const int b = bh / p.H, h = bh % p.H;
   const int hmi = p.hm == 1 ? 0 : h;
   const int Nq = p.Nq, Nk = p.Nk;
   const bool causal = p.causal != 0;
   const long long qslice = (long long)bh * Nq, kslice = (long long)bh * Nk;
-  const int c0 = kb * BKC, c1 = min(Nk, c0 + BKC);
-  const int wc0 = c0 + KW * w;
+  const int c0 = kb * C::BKC, c1 = min(Nk, c0 + C::BKC);
+  const int wc0 = c0 + 16 * w;
   const int j = wc0 + n16;   // this lane's key
-  const T* qg = reinterpret_cast<const T*>(p.q) + qslice * D;
-  const T* dog = reinterpret_cast<const T*>(p.dout) + qslice * DV;
+  if (tid < 3) wcount_[tid] = 0;
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(uniform_ptr(reinterpret_cast<const T*>(p.q) + qslice * D), (uint32_t)Nq * (uint32_t)(C::CPQ * 16));
+  const __amdgpu_buffer_rsrc_t rdo =
+      make_rsrc(uniform_ptr(reinterpret_cast<const T*>(p.dout) + qslice * DV), (uint32_t)Nq * (uint32_t)(C::CPO * 16));
+  // wave 0 moves each step's LSE2 values, wave 1 its delta values
+  const __amdgpu_buffer_rsrc_t rrow = make_rsrc(uniform_ptr(w == 0 ? p.lse2 + qslice : p.delta + qslice),
+                                                (uint32_t)Nq * 4u);
 
-  // the key's rows as B operands: step c holds [c KC + g KC / 4, + KC / 4)
+  // the key's rows as B operands
   typename X::op kr[D / KC], vr[DV / KC];
-  {
-    const T* kg = reinterpret_cast<const T*>(p.k) + kslice * D;
-    const T* vg = reinterpret_cast<const T*>(p.v) + kslice * DV;
-    const bool ok = j < Nk;
-#pragma unroll
-    for (int c = 0; c < D / KC; ++c) {
-      if constexpr (std::is_same<T, float>::value) {
-        kr[c] = ok ? kg[(long long)j * D + 4 * c + g] : 0.f;
-      } else {
-        kr[c] = ok ? *reinterpret_cast<const bf16x8*>(kg + (long long)j * D + 32 * c + 8 * g) : bf16x8{};
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < DV / KC; ++c) {
-      if constexpr (std::is_same<T, float>::value) {
-        vr[c] = ok ? vg[(long long)j * DV + 4 * c + g] : 0.f;
-      } else {
-        vr[c] = ok ? *reinterpret_cast<const bf16x8*>(vg + (long long)j * DV + 32 * c + 8 * g) : bf16x8{};
-      }
-    }
-  }
+  load_row_ops<T, D>(kr, reinterpret_cast<const T*>(p.k) + kslice * D, j, Nk, g);
+  load_row_ops<T, DV>(vr, reinterpret_cast<const T*>(p.v) + kslice * DV, j, Nk, g);
   const long long vrow = ((long long)b * p.hm + hmi) * Nk;
   int k_lts = 0, k_lte = 0, k_uts = 0, k_ute = 0;
   if (j < Nk) {
@@ -606,150 +682,182 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
       k_ute = p.ute[vrow + j];
     }
   }
-  constexpr int NKB = KCK / 16, NVB = KCV / 16;   // 16-column blocks of the chunk
-  f32x4 dkacc[NKB], dvacc[NVB];
+  f32x4 dkacc[KCK / 16], dvacc[KCV / 16];
 #pragma unroll
-  for (int mb = 0; mb < NKB; ++mb) dkacc[mb] = f32x4{};
+  for (int mb = 0; mb < KCK / 16; ++mb) dkacc[mb] = f32x4{};
 #pragma unroll
-  for (int mb = 0; mb < NVB; ++mb) dvacc[mb] = f32x4{};
+  for (int mb = 0; mb < KCV / 16; ++mb) dvacc[mb] = f32x4{};
   // bounds of the workgroup's 64 keys (one table entry); a wave's 16 keys
   // lie inside them, so the same bounds classify its part (possibly as
   // partial where its own keys alone would not be)
   const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb64 * 8;
   const BlockBounds kbnd = load_bounds(table + (long long)kb * 8);
-  unsigned cnt0 = 0, cnt1 = 0, cnt2 = 0;
+  unsigned cnt3[3] = {0u, 0u, 0u};
 
-  for (int qb = 0; qb < p.nqb; ++qb) {
-    const int q0 = qb * BQ, q1 = min(Nq, q0 + BQ);
+  auto cls = [&](int t, unsigned& bits) {
+    const int q0 = 32 * t, q1 = min(Nq, q0 + 32);
     const int wgc = tile_class(kbnd, q0, q1, c0, c1, causal);
-    cnt0 += wgc == 0;
-    cnt1 += wgc == 1;
-    cnt2 += wgc == 2;
-    if (wgc == 0) continue;
-    int wc = 0;
-    if (wc0 < Nk) {
-      wc = tile_class(kbnd, q0, q1, wc0, min(Nk, wc0 + KW), causal);
-      if (wc == 2 && (q1 - q0 < BQ || c1 - c0 < BKC)) wc = 1;
+    if (ch == 0) {   // column chunks share their steps: count them once
+      cnt3[0] += wgc == 0;
+      cnt3[1] += wgc == 1;
+      cnt3[2] += wgc == 2;
     }
-    __syncthreads();   // the last step's readers are done
-    stage<T, BQ, D>(qs, QS, qg, D, 0, q0, Nq);
-    stage<T, BQ, DV>(dos, OS, dog, DV, 0, q0, Nq);
-    if (tid < BQ) {
-      const bool ok = q0 + tid < Nq;
-      lse_s[tid] = ok ? p.lse2[qslice + q0 + tid] : __builtin_inff();
-      del_s[tid] = ok ? p.delta[qslice + q0 + tid] : 0.f;
-    }
-    __syncthreads();
-    if (wc == 0) continue;
-    // S = Q K^T and dP = dO V^T for the step's two 16-row halves (lane:
-    // key j; rows 16 mt + 4 g + e); the two chains alternate while both
-    // have steps left (D / KC and DV / KC of them)
-    constexpr int NSS = D / KC, NSD = DV / KC, NSMIN = NSS < NSD ? NSS : NSD;
-    auto is_dp = [](int t) { return t < 2 * NSMIN ? (t & 1) != 0 : NSD > NSS; };
-    auto sstep = [](int t) { return t < 2 * NSMIN ? t >> 1 : t - NSMIN; };
-    f32x4 s[2], dp[2];
+    if (wgc == 0) return 0;
+    const bool ragged = q1 - q0 < 32 || c1 - c0 < C::BKC;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = f32x4{};
-      dp[mt] = f32x4{};
-      chain<NSS + NSD, 2>(
-          [&](int t) {
-            return is_dp(t) ? row_op16<T>(dos, OS, 16 * mt + n16, sstep(t), g)
-                            : row_op16<T>(qs, QS, 16 * mt + n16, sstep(t), g);
-          },
-          [&](int t, typename X::op a) {
-            if (is_dp(t)) dp[mt] = X::mma(a, vr[sstep(t)], dp[mt]);
-            else s[mt] = X::mma(a, kr[sstep(t)], s[mt]);
-          });
-    }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int il = 16 * mt + 4 * g + e;
-        const bool m = (wc == 1) & hidden(p, q0 + il, j, k_lts, k_lte, k_uts, k_ute);
-        const float sv = m ? kNegInf : s[mt][e];
-        const float pv = exp2f(__builtin_fmaf(sv, p.sl2, -lse_s[il]));
-        s[mt][e] = pv;
-        dp[mt][e] = pv * (dp[mt][e] - del_s[il]);   // dS; the scale goes on dK at the end
+    for (int ww = 0; ww < 4; ++ww) {
+      const int a0 = c0 + 16 * ww;
+      int cl = 0;
+      if (a0 < Nk) {
+        cl = tile_class(kbnd, q0, q1, a0, min(Nk, a0 + 16), causal);
+        if (ragged && cl == 2) cl = 1;
       }
-    // P and dS as operands once (bf16: rounded), then dV^T += dO^T P and
-    // dK^T += Q^T dS over the step's 32 rows, the two products alternating
-    // while both have steps left; step u of a product is column block
-    // u / NST, row step u % NST
-    constexpr int NST = 32 / KC;
-    typename X::op pop[NST], dsop[NST];
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      pop[st] = acc_op16<T>(s, st);
-      dsop[st] = acc_op16<T>(dp, st);
+      bits |= (unsigned)cl << (2 * ww);
     }
-    constexpr int NMIN = (NKB < NVB ? NKB : NVB) * NST;
-    auto is_k = [](int t) { return t < 2 * NMIN ? (t & 1) != 0 : NKB > NVB; };
-    auto step_of = [](int t) { return t < 2 * NMIN ? t >> 1 : t - NMIN; };
-    chain<(NKB + NVB) * NST, 2>(
+    return wgc;
+  };
+
+  auto issue = [&](unsigned entry, auto stage_c) {
+    FM_LDS char* st = (FM_LDS char*)(decltype(stage_c)::value ? stage1 : stage0);
+    const int q0 = (int)(entry & 0xFFFFFFu) * C::BQ;
+    dma_rows<C::CPQ>(rq, st, C::RSQ, q0, w, lane);
+    dma_rows<C::CPO>(rdo, st + C::QT, C::RSO, q0, w, lane);
+    if (w < 2 && lane < 8) load_lds16(rrow, st + C::QT + C::OT + w * C::BQ * 4, (uint32_t)(q0 + 4 * lane) * 4u);
+  };
+
+  auto compute = [&](unsigned entry, auto stage_c) {
+    const int wc = (int)((entry >> (24 + 2 * w)) & 3u);
+    if (wc == 0) return;
+    const FM_LDS char* qst = (const FM_LDS char*)(decltype(stage_c)::value ? stage1 : stage0);
+    const FM_LDS char* dost = qst + C::QT;
+    const FM_LDS float* lse_l = (const FM_LDS float*)(qst + C::QT + C::OT);
+    const FM_LDS float* del_l = lse_l + C::BQ;
+    const int q0 = (int)(entry & 0xFFFFFFu) * C::BQ;
+    // S and dP for the step's two 16-row halves (lane: key j; rows
+    // 16 mt + 4 g + e), the two products alternating while both have steps
+    // left
+    constexpr int NS = 2 * (D / KC), ND = 2 * (DV / KC), NMIN = NS < ND ? NS : ND;
+    auto is_dp = [](int t) { return t < 2 * NMIN ? (t & 1) != 0 : ND > NS; };
+    auto ustep = [](int t) { return t < 2 * NMIN ? t >> 1 : t - NMIN; };
+    f32x4 s[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
+    chain<NS + ND, PF>(
         [&](int t) {
-          const int u = step_of(t), mb = u / NST, st = u % NST;
-          return is_k(t) ? col_op16<T>(qs, QS, ch * KCK + 16 * mb + n16, st, g)
-                         : col_op16<T>(dos, OS, ch * KCV + 16 * mb + n16, st, g);
+          const int u = ustep(t);
+          return is_dp(t) ? row_op<T>(dost, C::RSO, 16 * (u & 1) + n16, u >> 1, g)
+                          : row_op<T>(qst, C::RSQ, 16 * (u & 1) + n16, u >> 1, g);
         },
         [&](int t, typename X::op a) {
-          const int u = step_of(t), mb = u / NST, st = u % NST;
-          if (is_k(t)) dkacc[mb] = X::mma(a, dsop[st], dkacc[mb]);
-          else dvacc[mb] = X::mma(a, pop[st], dvacc[mb]);
+          const int u = ustep(t);
+          if (is_dp(t)) dp[u & 1] = X::mma(a, vr[u >> 1], dp[u & 1]);
+          else s[u & 1] = X::mma(a, kr[u >> 1], s[u & 1]);
         });
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int il = 16 * mt + 4 * g;
+      const f32x4 lse4 = *reinterpret_cast<const FM_LDS f32x4*>(lse_l + il);
+      const f32x4 del4 = *reinterpret_cast<const FM_LDS f32x4*>(del_l + il);
+      f32x4 pv4, ds4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool m = (wc == 1) & hidden(p, q0 + il + e, j, k_lts, k_lte, k_uts, k_ute);
+        const float sv = m ? kNegInf : s[mt][e];
+        const float pv = fast_exp2(__builtin_fmaf(sv, p.sl2, -lse4[e]));
+        pv4[e] = pv;
+        ds4[e] = pv * (dp[mt][e] - del4[e]);   // dS; the scale goes on dK at the end
+      }
+      s[mt] = pv4;
+      dp[mt] = ds4;
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the step's 32 rows (this
+    // chunk's columns), the two products alternating while both have steps
+    // left; step u of a product is column block u % NB, row step u / NB
+    constexpr int NST = 32 / KC, NKB = KCK / 16, NVB = KCV / 16;
+    constexpr int NK = NKB * NST, NV = NVB * NST, NM = NK < NV ? NK : NV;
+    auto is_k = [](int t) { return t < 2 * NM ? (t & 1) != 0 : NK > NV; };
+    auto kstep = [](int t) { return t < 2 * NM ? t >> 1 : t - NM; };
+    if constexpr (std::is_same<T, float>::value) {
+      chain<NK + NV, PF>(
+          [&](int t) {
+            const int u = kstep(t);
+            return is_k(t) ? col_f32(qst, C::RSQ, ch * KCK + 16 * (u % NKB) + n16, u / NKB, g)
+                           : col_f32(dost, C::RSO, ch * KCV + 16 * (u % NVB) + n16, u / NVB, g);
+          },
+          [&](int t, float a) {
+            const int u = kstep(t);
+            if (is_k(t)) dkacc[u % NKB] = X::mma(a, acc_op<T>(dp, u / NKB), dkacc[u % NKB]);
+            else dvacc[u % NVB] = X::mma(a, acc_op<T>(s, u / NVB), dvacc[u % NVB]);
+          });
+    } else {
+      const bf16x8 pop = acc_op<T>(s, 0), dsop = acc_op<T>(dp, 0);
+      chain<NK + NV, PF>(
+          [&](int t) {
+            const int u = kstep(t);
+            return is_k(t) ? col_tr(qst, C::RSQ, ch * KCK + 16 * u, lane)
+                           : col_tr(dost, C::RSO, ch * KCV + 16 * u, lane);
+          },
+          [&](int t, bf16x8 a) {
+            const int u = kstep(t);
+            if (is_k(t)) dkacc[u] = X::mma(a, dsop, dkacc[u]);
+            else dvacc[u] = X::mma(a, pop, dvacc[u]);
+          });
+    }
+  };
+
+  const int nqt = (Nq + C::BQ - 1) / C::BQ;
+  int cnt = 0;
+  for (int base = 0; base < nqt; base += 256) {
+    cnt = scan_chunk(list, (FM_LDS int*)wsum_, cnt, base, nqt, cls);
+    if (cnt > C::LIST - 256 || base + 256 >= nqt) {
+      run_list(list, cnt, issue, compute);
+      cnt = 0;
+    }
   }
 
   // lane: key j, dK columns ch KCK + 16 mb + 4 g + e, dV columns ch KCV + ...
   if (j < Nk) {
-    T* dkg = reinterpret_cast<T*>(p.dk) + (kslice + j) * D + ch * KCK;
-    T* dvg = reinterpret_cast<T*>(p.dv) + (kslice + j) * DV + ch * KCV;
+    T* dkg = reinterpret_cast<T*>(p.dk) + (kslice + j) * D + ch * KCK + 4 * g;
+    T* dvg = reinterpret_cast<T*>(p.dv) + (kslice + j) * DV + ch * KCV + 4 * g;
 #pragma unroll
-    for (int mb = 0; mb < NKB; ++mb) {
+    for (int mb = 0; mb < KCK / 16; ++mb) {
       if constexpr (std::is_same<T, float>::value) {
-        *reinterpret_cast<f32x4*>(dkg + 16 * mb + 4 * g) = dkacc[mb] * p.scale;
+        *reinterpret_cast<f32x4*>(dkg + 16 * mb) = dkacc[mb] * p.scale;
       } else {
         bf16x4 k4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) k4[e] = (bf16)(dkacc[mb][e] * p.scale);
-        *reinterpret_cast<bf16x4*>(dkg + 16 * mb + 4 * g) = k4;
+        *reinterpret_cast<bf16x4*>(dkg + 16 * mb) = k4;
       }
     }
 #pragma unroll
-    for (int mb = 0; mb < NVB; ++mb) {
+    for (int mb = 0; mb < KCV / 16; ++mb) {
       if constexpr (std::is_same<T, float>::value) {
-        *reinterpret_cast<f32x4*>(dvg + 16 * mb + 4 * g) = dvacc[mb];
+        *reinterpret_cast<f32x4*>(dvg + 16 * mb) = dvacc[mb];
       } else {
         bf16x4 v4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v4[e] = (bf16)dvacc[mb][e];
-        *reinterpret_cast<bf16x4*>(dvg + 16 * mb + 4 * g) = v4;
+        *reinterpret_cast<bf16x4*>(dvg + 16 * mb) = v4;
       }
     }
   }
-  if (ch == 0 && p.counts != nullptr && tid == 0) {
-    atomicAdd(p.counts + 0, (unsigned long long)cnt0);
-    atomicAdd(p.counts + 1, (unsigned long long)cnt1);
-    atomicAdd(p.counts + 2, (unsigned long long)cnt2);
-  }
+  flush_counts(p.counts, wcount_, cnt3);
 }
 
 // ---------------------------------------------------------------- launch
-// Column chunks per shape: the forward's O chunk (DVC columns), the dQ
-// pass's dQ chunk (DC) and the number of dK/dV chunks (NCH).
+// dK/dV column chunks per shape
 template <typename T, int D, int DV>
 struct WideCfg;
 template <>
 struct WideCfg<bf16, 512, 512> {
-  static constexpr int DVC = 256, DC = 128, NCH = 2;
+  static constexpr int NCH = 2;
 };
 template <>
 struct WideCfg<float, 256, 256> {
-  static constexpr int DVC = 256, DC = 128, NCH = 1;
+  static constexpr int NCH = 1;
 };
 template <>
 struct WideCfg<float, 192, 128> {
-  static constexpr int DVC = 128, DC = 192, NCH = 1;
+  static constexpr int NCH = 1;
 };
 
 static WideParams wide_params(const AttnArgs& a) {
@@ -789,11 +897,10 @@ static WideParams wide_params(const AttnArgs& a) {
 
 template <typename T, int D, int DV>
 static hipError_t launch_wide_fwd_t(const AttnArgs& a, hipStream_t stream) {
-  using C = WideCfg<T, D, DV>;
   WideParams p = wide_params(a);
-  p.nqb = (a.Nq + 127) / 128;
-  const long long grid = (long long)a.B * a.H * p.nqb * (DV / C::DVC);
-  hipLaunchKernelGGL((wide_fwd_kernel<T, D, DV, C::DVC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  p.nqb = (a.Nq + 63) / 64;
+  const long long grid = (long long)a.B * a.H * p.nqb;
+  hipLaunchKernelGGL((wide_fwd_kernel<T, D, DV>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -802,12 +909,11 @@ static hipError_t launch_wide_bwd_t(const AttnArgs& a, hipStream_t stream) {
   using C = WideCfg<T, D, DV>;
   WideParams p = wide_params(a);
   p.pdsum = a.sink != nullptr ? a.pdsum : nullptr;
-  p.nqb = (a.Nq + 127) / 128;
-  long long grid = (long long)a.B * a.H * p.nqb * (D / C::DC);
-  hipLaunchKernelGGL((wide_dq_kernel<T, D, DV, C::DC>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  p.nqb = (a.Nq + 63) / 64;
+  long long grid = (long long)a.B * a.H * p.nqb;
+  hipLaunchKernelGGL((wide_dq_kernel<T, D, DV>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  p.nqb = (a.Nq + 31) / 32;
   grid = (long long)a.B * a.H * p.nkb64 * C::NCH;
   hipLaunchKernelGGL((wide_dkdv_kernel<T, D, DV, C::NCH>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
