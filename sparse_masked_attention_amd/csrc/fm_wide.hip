@@ -608,14 +608,15 @@ __global__ __launch_bounds__(256, 1) void wide_dq_kernel(WideParams p) {
 }
 
 // ---------------------------------------------------------------- dK/dV pass
-// Workgroup: 64 keys (16 per wave), chunk ch of NCH: dK columns
-// [ch KCK, (ch + 1) KCK) and dV columns [ch KCV, (ch + 1) KCV), KCK = D / NCH,
-// KCV = DV / NCH. K and V rows of the lane's key in registers; per visible
-// 32-row query step (Q, dO, LSE2 and delta in LDS):
+// Workgroup: 64 keys (16 per wave), every dK and dV column. K and V rows of
+// the lane's key in registers; per visible 32-row query step (Q, dO, LSE2
+// and delta in LDS):
 //   S = Q K^T, dP = dO V^T, the mask from the key's own bounds,
 //   P = exp2(S scale log2e - LSE2), dS = P (dP - delta),
-//   dV^T += dO^T P and dK^T += Q^T dS (this chunk's columns; dK takes the
-//   scale once, at the end).
+//   dV^T += dO^T P and dK^T += Q^T dS (dK takes the scale once, at the end).
+// At d = dv = 512 the key's operands (128 registers) and the dK and dV
+// accumulators (256) fill most of a lane's 512; one 8-byte value of the
+// prologue goes to scratch until the epilogue.
 template <typename T, int D, int DV>
 struct WKv {
   static constexpr int BKC = 64, BQ = 32;
@@ -627,13 +628,11 @@ struct WKv {
   static constexpr int LIST = 512;
 };
 
-template <typename T, int D, int DV, int NCH>
+template <typename T, int D, int DV>
 __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
   using X = W16<T>;
   using C = WKv<T, D, DV>;
-  constexpr int KCK = D / NCH, KCV = DV / NCH;
-  static_assert(KCK * NCH == D && KCV * NCH == DV && KCK % 16 == 0 && KCV % 16 == 0, "column chunks");
-  constexpr int KC = X::KC, PF = 6;
+  constexpr int KC = X::KC, PF = 4;
   __shared__ __attribute__((aligned(16))) char stage0[C::STAGE];
   __shared__ __attribute__((aligned(16))) char stage1[C::STAGE];
   __shared__ int list_[C::LIST];
@@ -646,9 +645,8 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
   const int w = uniform(tid >> 6);
   const int g = lane >> 4, n16 = lane & 15;
   const int BH = p.B * p.H;
-  const int ch = (int)(blockIdx.x % NCH);
   int bh, kb;
-  xcd_order((int)(blockIdx.x / NCH), BH, p.nkb64, bh, kb);   // early (heavy) key blocks first
+  xcd_order((int)blockIdx.x, BH, p.nkb64, bh, kb);   // early (heavy) key blocks first
   const int b = bh / p.H, h = bh % p.H;
   const int hmi = p.hm == 1 ? 0 : h;
   const int Nq = p.Nq, Nk = p.Nk;
@@ -682,11 +680,11 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
       k_ute = p.ute[vrow + j];
     }
   }
-  f32x4 dkacc[KCK / 16], dvacc[KCV / 16];
+  f32x4 dkacc[D / 16], dvacc[DV / 16];
 #pragma unroll
-  for (int mb = 0; mb < KCK / 16; ++mb) dkacc[mb] = f32x4{};
+  for (int mb = 0; mb < D / 16; ++mb) dkacc[mb] = f32x4{};
 #pragma unroll
-  for (int mb = 0; mb < KCV / 16; ++mb) dvacc[mb] = f32x4{};
+  for (int mb = 0; mb < DV / 16; ++mb) dvacc[mb] = f32x4{};
   // bounds of the workgroup's 64 keys (one table entry); a wave's 16 keys
   // lie inside them, so the same bounds classify its part (possibly as
   // partial where its own keys alone would not be)
@@ -697,11 +695,9 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
   auto cls = [&](int t, unsigned& bits) {
     const int q0 = 32 * t, q1 = min(Nq, q0 + 32);
     const int wgc = tile_class(kbnd, q0, q1, c0, c1, causal);
-    if (ch == 0) {   // column chunks share their steps: count them once
-      cnt3[0] += wgc == 0;
-      cnt3[1] += wgc == 1;
-      cnt3[2] += wgc == 2;
-    }
+    cnt3[0] += wgc == 0;
+    cnt3[1] += wgc == 1;
+    cnt3[2] += wgc == 2;
     if (wgc == 0) return 0;
     const bool ragged = q1 - q0 < 32 || c1 - c0 < C::BKC;
 #pragma unroll
@@ -768,10 +764,10 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
       s[mt] = pv4;
       dp[mt] = ds4;
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over the step's 32 rows (this
-    // chunk's columns), the two products alternating while both have steps
-    // left; step u of a product is column block u % NB, row step u / NB
-    constexpr int NST = 32 / KC, NKB = KCK / 16, NVB = KCV / 16;
+    // dV^T += dO^T P and dK^T += Q^T dS over the step's 32 rows, the two
+    // products alternating while both have steps left; step u of a product
+    // is column block u % NB, row step u / NB
+    constexpr int NST = 32 / KC, NKB = D / 16, NVB = DV / 16;
     constexpr int NK = NKB * NST, NV = NVB * NST, NM = NK < NV ? NK : NV;
     auto is_k = [](int t) { return t < 2 * NM ? (t & 1) != 0 : NK > NV; };
     auto kstep = [](int t) { return t < 2 * NM ? t >> 1 : t - NM; };
@@ -779,8 +775,8 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
       chain<NK + NV, PF>(
           [&](int t) {
             const int u = kstep(t);
-            return is_k(t) ? col_f32(qst, C::RSQ, ch * KCK + 16 * (u % NKB) + n16, u / NKB, g)
-                           : col_f32(dost, C::RSO, ch * KCV + 16 * (u % NVB) + n16, u / NVB, g);
+            return is_k(t) ? col_f32(qst, C::RSQ, 16 * (u % NKB) + n16, u / NKB, g)
+                           : col_f32(dost, C::RSO, 16 * (u % NVB) + n16, u / NVB, g);
           },
           [&](int t, float a) {
             const int u = kstep(t);
@@ -792,8 +788,7 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
       chain<NK + NV, PF>(
           [&](int t) {
             const int u = kstep(t);
-            return is_k(t) ? col_tr(qst, C::RSQ, ch * KCK + 16 * u, lane)
-                           : col_tr(dost, C::RSO, ch * KCV + 16 * u, lane);
+            return is_k(t) ? col_tr(qst, C::RSQ, 16 * u, lane) : col_tr(dost, C::RSO, 16 * u, lane);
           },
           [&](int t, bf16x8 a) {
             const int u = kstep(t);
@@ -813,12 +808,12 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
     }
   }
 
-  // lane: key j, dK columns ch KCK + 16 mb + 4 g + e, dV columns ch KCV + ...
+  // lane: key j, dK and dV columns 16 mb + 4 g + e
   if (j < Nk) {
-    T* dkg = reinterpret_cast<T*>(p.dk) + (kslice + j) * D + ch * KCK + 4 * g;
-    T* dvg = reinterpret_cast<T*>(p.dv) + (kslice + j) * DV + ch * KCV + 4 * g;
+    T* dkg = reinterpret_cast<T*>(p.dk) + (kslice + j) * D + 4 * g;
+    T* dvg = reinterpret_cast<T*>(p.dv) + (kslice + j) * DV + 4 * g;
 #pragma unroll
-    for (int mb = 0; mb < KCK / 16; ++mb) {
+    for (int mb = 0; mb < D / 16; ++mb) {
       if constexpr (std::is_same<T, float>::value) {
         *reinterpret_cast<f32x4*>(dkg + 16 * mb) = dkacc[mb] * p.scale;
       } else {
@@ -829,7 +824,7 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
       }
     }
 #pragma unroll
-    for (int mb = 0; mb < KCV / 16; ++mb) {
+    for (int mb = 0; mb < DV / 16; ++mb) {
       if constexpr (std::is_same<T, float>::value) {
         *reinterpret_cast<f32x4*>(dvg + 16 * mb) = dvacc[mb];
       } else {
@@ -844,21 +839,6 @@ __global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
 }
 
 // ---------------------------------------------------------------- launch
-// dK/dV column chunks per shape
-template <typename T, int D, int DV>
-struct WideCfg;
-template <>
-struct WideCfg<bf16, 512, 512> {
-  static constexpr int NCH = 2;
-};
-template <>
-struct WideCfg<float, 256, 256> {
-  static constexpr int NCH = 1;
-};
-template <>
-struct WideCfg<float, 192, 128> {
-  static constexpr int NCH = 1;
-};
 
 static WideParams wide_params(const AttnArgs& a) {
   WideParams p{};
@@ -906,7 +886,6 @@ static hipError_t launch_wide_fwd_t(const AttnArgs& a, hipStream_t stream) {
 
 template <typename T, int D, int DV>
 static hipError_t launch_wide_bwd_t(const AttnArgs& a, hipStream_t stream) {
-  using C = WideCfg<T, D, DV>;
   WideParams p = wide_params(a);
   p.pdsum = a.sink != nullptr ? a.pdsum : nullptr;
   p.nqb = (a.Nq + 63) / 64;
@@ -914,8 +893,8 @@ static hipError_t launch_wide_bwd_t(const AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((wide_dq_kernel<T, D, DV>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  grid = (long long)a.B * a.H * p.nkb64 * C::NCH;
-  hipLaunchKernelGGL((wide_dkdv_kernel<T, D, DV, C::NCH>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  grid = (long long)a.B * a.H * p.nkb64;
+  hipLaunchKernelGGL((wide_dkdv_kernel<T, D, DV>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
