@@ -110,19 +110,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // Key-major: a workgroup (4 waves) owns 128 keys, 32 per wave, and walks the
 // query blocks the mask leaves visible. K and V of the lane's key are MFMA B
 // operands held in registers; dK and dV accumulate in registers. dQ is not
-// formed here (the query-major dQ pass does it without atomics).
-// d = 256 does not fit dK and dV of 32 keys per wave in registers; it runs as
-// two workgroups per key block, each owning half of the dK/dV columns and
-// recomputing S and dP in full.
+// formed here (the query-major dQ pass does it without atomics). (At
+// d = dv = 256 the wide-head-dim kernels run the backward: dK and dV of 32
+// keys per wave do not fit this kernel's registers.)
 // D: head dim of Q and K (and dQ, dK); DV: head dim of V (and dO, dV).
 template <int D, int DV>
 struct BwdCfg {
   static constexpr int NW = 4;
   static constexpr int KW = 32;                 // keys per wave
   static constexpr int BKC = NW * KW;           // keys per workgroup
-  static constexpr int NSPLIT = D >= 256 ? 2 : 1;
-  static constexpr int DO = D / NSPLIT;         // dK columns per workgroup
-  static constexpr int DVO = DV / NSPLIT;       // dV columns per workgroup
 #ifdef FM_ALT_TILES
   static constexpr int BQ = 32;                 // query rows per step (second configuration)
 #else
@@ -139,8 +135,8 @@ struct BwdCfg {
   static constexpr int LOADS_PER_STEP = LOADS_Q + LOADS_O + 1;   // waves 0/1 add LSE2 / delta
   // Where a wave's 32 dK (and dV) rows fit a quarter of a stage, the rows go
   // out staged through LDS and the workgroups are persistent.
-  static constexpr bool PERSIST = DO == DVO && NW * KW * DO * 2 <= STAGE;
-  static constexpr int NSTORE = DO / 16 + DVO / 16;   // 16-byte row stores per lane of dK and dV
+  static constexpr bool PERSIST = D == DV && NW * KW * D * 2 <= STAGE;
+  static constexpr int NSTORE = D / 16 + DV / 16;   // 16-byte row stores per lane of dK and dV
 };
 
 // Chunk swizzle shared by row reads (32 rows, one chunk) and transposed reads
@@ -193,7 +189,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   if (tid < 3) wcount[tid] = 0;
   unsigned cnt0 = 0, cnt1 = 0, cnt2 = 0;
 
-  // --- work items: (head, 128-key block, dK/dV column half). Without
+  // --- work items: (head, 128-key block). Without
   // persistence, workgroup t does item t. Persistent workgroups (one per CU)
   // take items from work queues: queue qi holds the items t = n * nqueue + qi
   // in the order n = 0, 1, ..., which with 8 queues keeps every item of a
@@ -215,20 +211,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   }
 
   // per-item state
-  int bh, kb, sp, col0, col0v, c0, c1, wc0, j;
+  int bh, kb, c0, c1, wc0, j;
   long long qslice, kslice;
   __amdgpu_buffer_rsrc_t rq, rk, rv, rdo, rlse, rdel;
   const int32_t* table;
-  bool tail, count_item;
+  bool tail;
   int k_lts, k_lte, k_uts, k_ute;
   auto setup = [&](int it) {
-    int rest;
-    xcd_order(kPersist ? it * p.nqueue + qi : it, BH, p.nkb * C::NSPLIT, bh, rest);
-    kb = rest / C::NSPLIT;
-    sp = rest % C::NSPLIT;                 // which output column half
-    col0 = sp * C::DO;                     // first dK column of this item
-    col0v = sp * C::DVO;                   // first dV column
-    count_item = sp == 0;                  // column halves share their tiles: count them once
+    xcd_order(kPersist ? it * p.nqueue + qi : it, BH, p.nkb, bh, kb);
     const int b = bh / p.H, h = bh % p.H;
     const int hmi = p.hm == 1 ? 0 : h;
     qslice = (long long)bh * Nq;           // rows of Q, dO, LSE, delta
@@ -273,12 +263,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       vB[c] = __builtin_bit_cast(bf16x8, buffer_load16(rv, (uint32_t)(j * DV + 16 * c + 8 * hh) * 2));
   };
 
-  f32x16 dvacc[C::DVO / 32], dkacc[C::DO / 32];
+  f32x16 dvacc[DV / 32], dkacc[D / 32];
   auto zero_acc = [&]() {
 #pragma unroll
-    for (int mb = 0; mb < C::DVO / 32; ++mb) dvacc[mb] = f32x16{};
+    for (int mb = 0; mb < DV / 32; ++mb) dvacc[mb] = f32x16{};
 #pragma unroll
-    for (int mb = 0; mb < C::DO / 32; ++mb) dkacc[mb] = f32x16{};
+    for (int mb = 0; mb < D / 32; ++mb) dkacc[mb] = f32x16{};
   };
 
   auto issue = [&](unsigned entry, auto stage_c) {
@@ -398,7 +388,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     // dV += P^T dO and dK += dS^T Q over the 16-row chunks cc and cc + 1; the
     // dO / Q operands come by transposed reads, and dV and dK steps alternate
     // while both have steps left
-    constexpr int NV2 = C::DVO / 32, NK2 = C::DO / 32, NC = NV2 + NK2;
+    constexpr int NV2 = DV / 32, NK2 = D / 32, NC = NV2 + NK2;
     constexpr int NCMIN = NV2 < NK2 ? NV2 : NK2;
     static_assert(2 * NC >= PF, "prefetch ring deeper than the dV / dK steps");
     const int sl = lane & 15;
@@ -411,10 +401,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         const int ra = 16 * c + 4 * hh + (sl >> 2);
         const int rb = ra + 8;
         if (is_v(u)) {
-          const int col = col0v + 32 * mblk(u) + cl;
+          const int col = 32 * mblk(u) + cl;
           return cat(lds_read_tr(tile_addr<DV>(dost, ra, col)), lds_read_tr(tile_addr<DV>(dost, rb, col)));
         }
-        const int col = col0 + 32 * mblk(u) + cl;
+        const int col = 32 * mblk(u) + cl;
         return cat(lds_read_tr(tile_addr<D>(qst, ra, col)), lds_read_tr(tile_addr<D>(qst, rb, col)));
       };
       bf16x8 ring[PF];
@@ -480,11 +470,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       if (qb < p.nqb) {
         const int r0 = qb * C::BQ, r1 = min(Nq, r0 + C::BQ);
         const int wgc = tile_class(kbnd, r0, r1, c0, c1, causal);
-        if (count_item) {
-          cnt0 += wgc == 0;
-          cnt1 += wgc == 1;
-          cnt2 += wgc == 2;
-        }
+        cnt0 += wgc == 0;
+        cnt1 += wgc == 1;
+        cnt2 += wgc == 2;
         if (wgc != 0) {
           valid = true;
           const bool ragged = tail || (r1 - r0 < C::BQ);
@@ -605,11 +593,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           const int key = wc0 + 8 * (r / 4) + 4 * hh + (r % 4);
           if (key < Nk) {
 #pragma unroll
-            for (int mb = 0; mb < C::DO / 32; ++mb)
-              dkg[(long long)key * D + col0 + 32 * mb + l32] = (bf16)(dkacc[mb][r] * p.scale);
+            for (int mb = 0; mb < D / 32; ++mb)
+              dkg[(long long)key * D + 32 * mb + l32] = (bf16)(dkacc[mb][r] * p.scale);
 #pragma unroll
-            for (int mb = 0; mb < C::DVO / 32; ++mb)
-              dvg[(long long)key * DV + col0v + 32 * mb + l32] = (bf16)dvacc[mb][r];
+            for (int mb = 0; mb < DV / 32; ++mb)
+              dvg[(long long)key * DV + 32 * mb + l32] = (bf16)dvacc[mb][r];
           }
         }
       }
@@ -620,11 +608,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       // are dropped and every wave issues the same C::NSTORE stores.
       const int nrow = uniform(max(0, min(C::KW, Nk - wc0)));
       const __amdgpu_buffer_rsrc_t rdk =
-          make_rsrc(uniform_ptr(reinterpret_cast<bf16*>(p.dk) + (kslice + wc0) * D + col0),
-                    nrow > 0 ? (uint32_t)((nrow - 1) * D + C::DO) * 2 : 0u);
+          make_rsrc(uniform_ptr(reinterpret_cast<bf16*>(p.dk) + (kslice + wc0) * D),
+                    nrow > 0 ? (uint32_t)(nrow * D) * 2 : 0u);
       const __amdgpu_buffer_rsrc_t rdv =
-          make_rsrc(uniform_ptr(reinterpret_cast<bf16*>(p.dv) + (kslice + wc0) * DV + col0v),
-                    nrow > 0 ? (uint32_t)((nrow - 1) * DV + C::DVO) * 2 : 0u);
+          make_rsrc(uniform_ptr(reinterpret_cast<bf16*>(p.dv) + (kslice + wc0) * DV),
+                    nrow > 0 ? (uint32_t)(nrow * DV) * 2 : 0u);
       // the next item: its ticket is taken here (nothing else is in flight)
       __syncthreads();   // no wave still reads this item's list, stages or the last ticket
       if (tid == 0) next_item = atomicAdd(p.queue + qi, 1);
@@ -650,7 +638,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       // (free: the next item's first tiles are in stages 0 and 1). A lane
       // holds one column of 16 keys; staged, each store writes whole rows,
       // 16 bytes per lane.
-      FM_LDS char* est = (FM_LDS char*)stage2 + w * C::KW * C::DO * 2;
+      FM_LDS char* est = (FM_LDS char*)stage2 + w * C::KW * D * 2;
       // The lane index is re-derived here through an opaque copy: addresses
       // computed from it cannot then be hoisted above the tile loop, where
       // they would hold registers for the whole item.
@@ -666,12 +654,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           __builtin_amdgcn_raw_buffer_store_b128(val, r, (uint32_t)(row * ld + 8 * c) * 2, 0, 0);
         }
       };
-      stage_rows(est, dkacc, p.scale, elane >> 5, elane & 31, std::integral_constant<int, C::DO>{});
+      stage_rows(est, dkacc, p.scale, elane >> 5, elane & 31, std::integral_constant<int, D>{});
       __builtin_amdgcn_wave_barrier();
-      store_rows(rdk, D, std::integral_constant<int, C::DO>{});
-      stage_rows(est, dvacc, 1.f, elane >> 5, elane & 31, std::integral_constant<int, C::DVO>{});
+      store_rows(rdk, D, std::integral_constant<int, D>{});
+      stage_rows(est, dvacc, 1.f, elane >> 5, elane & 31, std::integral_constant<int, DV>{});
       __builtin_amdgcn_wave_barrier();
-      store_rows(rdv, DV, std::integral_constant<int, C::DVO>{});
+      store_rows(rdv, DV, std::integral_constant<int, DV>{});
       __builtin_amdgcn_sched_barrier(0);
       // the next item's first two tiles, K, V and key bounds have landed;
       // only the stores may be in flight. (Waited for on both paths, so that
@@ -873,7 +861,7 @@ static hipError_t launch_bwd_bf16(BwdParams p, const AttnArgs& a, hipStream_t st
   // the dQ pass also writes delta and the base-2 LSE the dK/dV pass reads
   const hipError_t e = launch_bwd_dq(a, stream);
   if (e != hipSuccess) return e;
-  const long long items = (long long)p.B * p.H * p.nkb * C::NSPLIT;
+  const long long items = (long long)p.B * p.H * p.nkb;
   long long grid = items;
   if constexpr (C::PERSIST) {
     // one workgroup per CU, 8 queues (one per XCD) when the heads split
@@ -1031,11 +1019,12 @@ static hipError_t launch_bwd_main(const AttnArgs& a, hipStream_t stream) {
   p.sl2 = a.scale * kLog2e;
   p.nkb = (a.Nk + kBwdBlockK - 1) / kBwdBlockK;
   p.nkb64 = (a.Nk + kTableBlock - 1) / kTableBlock;
-  if (wide_dims(a.d, a.dv, a.is_bf16)) {
+  if (wide_bwd_dims(a.d, a.dv, a.is_bf16)) {
     // delta and the base-2 LSE, then the wide dQ and dK/dV passes
     p.nqb = (p.Nq + 31) / 32;
     // (the preprocess reads rows of O and dO, dv wide)
-    const hipError_t e = a.is_bf16       ? launch_pre<512, bf16>(p, stream)
+    const hipError_t e = a.is_bf16   ? (a.dv == 512 ? launch_pre<512, bf16>(p, stream)
+                                                    : launch_pre<256, bf16>(p, stream))
                          : a.dv == 256 ? launch_pre<256, float>(p, stream)
                                        : launch_pre<128, float>(p, stream);
     if (e != hipSuccess) return e;
@@ -1045,7 +1034,6 @@ static hipError_t launch_bwd_main(const AttnArgs& a, hipStream_t stream) {
     // the bf16 (d, dv) pairs compiled in (kept in step with bf16_dims())
     if (a.d == 64 && a.dv == 64) return launch_bwd_bf16<64, 64>(p, a, stream);
     if (a.d == 128 && a.dv == 128) return launch_bwd_bf16<128, 128>(p, a, stream);
-    if (a.d == 256 && a.dv == 256) return launch_bwd_bf16<256, 256>(p, a, stream);
     if (a.d == 192 && a.dv == 128) return launch_bwd_bf16<192, 128>(p, a, stream);
   } else {
     switch (a.d) {

@@ -26,9 +26,9 @@ inline int bwd_block_q(int d, int is_bf16) { (void)d; (void)is_bf16; return 32; 
 inline int bwd_block_q(int d, int is_bf16) { return (is_bf16 && d <= 128) ? 64 : 32; }
 #endif
 // backward key-block width: 64 keys where the wide-head-dim kernels serve the
-// Q/K head dim d (bf16 512; fp32 256 and 192), else kBwdBlockK
+// backward at Q/K head dim d (bf16 512 and 256; fp32 256 and 192), else kBwdBlockK
 inline int bwd_block_k(int d, int is_bf16) {
-  return (is_bf16 ? d == 512 : (d == 256 || d == 192)) ? 64 : kBwdBlockK;
+  return (is_bf16 ? (d == 512 || d == 256) : (d == 256 || d == 192)) ? 64 : kBwdBlockK;
 }
 
 // Head dims with kernels compiled in: (d, dv) pairs for bf16, d == dv for fp32.
@@ -43,6 +43,11 @@ inline bool fp32_dims(int d, int dv) {
 inline bool wide_dims(int d, int dv, bool is_bf16) {
   if (is_bf16) return d == 512 && dv == 512;
   return (d == 256 && dv == 256) || (d == 192 && dv == 128);
+}
+// the backward also at bf16 d = dv = 256, where the wide kernels' dQ and
+// dK/dV passes (two workgroups per CU) beat the 32-row ones
+inline bool wide_bwd_dims(int d, int dv, bool is_bf16) {
+  return wide_dims(d, dv, is_bf16) || (is_bf16 && d == 256 && dv == 256);
 }
 
 struct MaskArgs {

@@ -1,5 +1,5 @@
 // Wide head dims: bf16 with d = dv = 512, fp32 with d = dv = 256 and with
-// (d, dv) = (192, 128).
+// (d, dv) = (192, 128); and the backward at bf16 d = dv = 256.
 //
 // The pages list large head dims among the method's features (FlashMask
 // README, "News" and "Key Features"); the computation is the same as at
@@ -25,7 +25,9 @@
 // forward and dQ pass, key-major dK/dV pass, each tile classified from the
 // key-block table). Tiles of 32 rows move into LDS by LDS DMA (one 16-byte
 // piece per lane, one instruction per tile row), two stages deep: the next
-// visible tile loads while the current one is computed.
+// visible tile loads while the current one is computed. With rows of at most
+// 512 bytes (bf16 d = 256) two workgroups share a CU; wider rows take a CU
+// each.
 #include <type_traits>
 
 #include "fm_device.hpp"
@@ -57,6 +59,13 @@ struct WideParams {
   float scale, sl2;
   int nqb, nkb64;   // query blocks (or steps); 64-key table entries
 };
+
+// Waves per SIMD a kernel is built for: 2 (two workgroups per CU, at most 256
+// registers per lane) where rows are at most 512 bytes, else 1.
+template <typename T, int D, int DV>
+constexpr int wide_occupancy() {
+  return (int)sizeof(T) * D <= 512 && (int)sizeof(T) * DV <= 512 ? 2 : 1;
+}
 
 // ---------------------------------------------------------------- MFMA forms
 template <typename T>
@@ -323,7 +332,7 @@ __device__ inline void flush_counts(unsigned long long* counts, unsigned* wcount
 }
 
 template <typename T, int D, int DV>
-__global__ __launch_bounds__(256, 1) void wide_fwd_kernel(WideParams p) {
+__global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_fwd_kernel(WideParams p) {
   using X = W16<T>;
   using C = WFwd<T, D, DV>;
   constexpr int KC = X::KC, PF = 6;
@@ -478,7 +487,7 @@ struct WDq {
 };
 
 template <typename T, int D, int DV>
-__global__ __launch_bounds__(256, 1) void wide_dq_kernel(WideParams p) {
+__global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_dq_kernel(WideParams p) {
   using X = W16<T>;
   using C = WDq<T, D, DV>;
   constexpr int KC = X::KC, PF = 6;
@@ -629,7 +638,7 @@ struct WKv {
 };
 
 template <typename T, int D, int DV>
-__global__ __launch_bounds__(256, 1) void wide_dkdv_kernel(WideParams p) {
+__global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_dkdv_kernel(WideParams p) {
   using X = W16<T>;
   using C = WKv<T, D, DV>;
   constexpr int KC = X::KC, PF = 4;
@@ -898,7 +907,7 @@ static hipError_t launch_wide_bwd_t(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// the shapes compiled in (kept in step with wide_dims())
+// the shapes compiled in (kept in step with wide_dims() and wide_bwd_dims())
 hipError_t launch_wide_fwd(const AttnArgs& a, hipStream_t stream) {
   if (a.is_bf16 && a.d == 512 && a.dv == 512) return launch_wide_fwd_t<bf16, 512, 512>(a, stream);
   if (!a.is_bf16 && a.d == 256 && a.dv == 256) return launch_wide_fwd_t<float, 256, 256>(a, stream);
@@ -908,6 +917,7 @@ hipError_t launch_wide_fwd(const AttnArgs& a, hipStream_t stream) {
 
 hipError_t launch_wide_bwd(const AttnArgs& a, hipStream_t stream) {
   if (a.is_bf16 && a.d == 512 && a.dv == 512) return launch_wide_bwd_t<bf16, 512, 512>(a, stream);
+  if (a.is_bf16 && a.d == 256 && a.dv == 256) return launch_wide_bwd_t<bf16, 256, 256>(a, stream);
   if (!a.is_bf16 && a.d == 256 && a.dv == 256) return launch_wide_bwd_t<float, 256, 256>(a, stream);
   if (!a.is_bf16 && a.d == 192 && a.dv == 128) return launch_wide_bwd_t<float, 192, 128>(a, stream);
   return hipErrorInvalidValue;
