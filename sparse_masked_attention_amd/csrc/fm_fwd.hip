@@ -475,7 +475,7 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
         }
       };
       if constexpr (D > 128) {
-        s_chain(std::true_type{});   // one chain (two spill at d = 256)
+        s_chain(std::true_type{});   // one chain above d = 128, where registers are short
       } else {
         if (wc == 1) s_chain(std::true_type{});
         else s_chain(std::false_type{});
@@ -919,9 +919,6 @@ template <int MODE>
 static hipError_t dispatch_qmajor(int d, int dv, const FwdParams& p, hipStream_t stream) {
   if (d == 64 && dv == 64) return launch_qmajor<64, 64, MODE>(p, stream);
   if (d == 128 && dv == 128) return launch_qmajor<128, 128, MODE>(p, stream);
-  if constexpr (MODE == kModeFwd) {   // (the bf16 d = 256 backward runs the wide-head-dim kernels)
-    if (d == 256 && dv == 256) return launch_qmajor<256, 256, MODE>(p, stream);
-  }
   if (d == 192 && dv == 128) return launch_qmajor<192, 128, MODE>(p, stream);
   return hipErrorInvalidValue;
 }

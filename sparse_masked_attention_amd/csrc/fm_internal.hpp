@@ -12,11 +12,9 @@ constexpr int kTableBlock = 64;
 
 // Tile shapes the attention kernels classify (query rows x key columns).
 constexpr int kFwdBlockK = 64;
-// forward query-block height: 4 waves x 32 rows, or 4 x 16 where the
-// wide-head-dim kernels serve the Q/K head dim d (bf16 512; fp32 256 and 192)
-inline int fwd_block_q(int d, int is_bf16) {
-  return (is_bf16 ? d == 512 : (d == 256 || d == 192)) ? 64 : 128;
-}
+// forward query-block height: 4 waves x 32 rows (4 x 16 in the wide-head-dim
+// forward at bf16 d = 512)
+inline int fwd_block_q(int d, int is_bf16) { return is_bf16 && d == 512 ? 64 : 128; }
 constexpr int kBwdBlockK = 128;
 // backward query-block height: 64 rows for bf16 with d <= 128, else 32 (32
 // everywhere in the second tile configuration, FM_ALT_TILES)
@@ -26,7 +24,7 @@ inline int bwd_block_q(int d, int is_bf16) { (void)d; (void)is_bf16; return 32; 
 inline int bwd_block_q(int d, int is_bf16) { return (is_bf16 && d <= 128) ? 64 : 32; }
 #endif
 // backward key-block width: 64 keys where the wide-head-dim kernels serve the
-// backward at Q/K head dim d (bf16 512 and 256; fp32 256 and 192), else kBwdBlockK
+// Q/K head dim d (bf16 512 and 256; fp32 256 and 192), else kBwdBlockK
 inline int bwd_block_k(int d, int is_bf16) {
   return (is_bf16 ? (d == 512 || d == 256) : (d == 256 || d == 192)) ? 64 : kBwdBlockK;
 }
@@ -39,15 +37,10 @@ inline bool fp32_dims(int d, int dv) {
   return (d == dv && (d == 64 || d == 128 || d == 256)) || (d == 192 && dv == 128);
 }
 // the shapes served by the wide-head-dim kernels of fm_wide.hip: bf16
-// d = dv = 512; fp32 d = dv = 256 and (d, dv) = (192, 128)
+// d = dv = 512 and 256; fp32 d = dv = 256 and (d, dv) = (192, 128)
 inline bool wide_dims(int d, int dv, bool is_bf16) {
-  if (is_bf16) return d == 512 && dv == 512;
+  if (is_bf16) return (d == 512 && dv == 512) || (d == 256 && dv == 256);
   return (d == 256 && dv == 256) || (d == 192 && dv == 128);
-}
-// the backward also at bf16 d = dv = 256, where the wide kernels' dQ and
-// dK/dV passes (two workgroups per CU) beat the 32-row ones
-inline bool wide_bwd_dims(int d, int dv, bool is_bf16) {
-  return wide_dims(d, dv, is_bf16) || (is_bf16 && d == 256 && dv == 256);
 }
 
 struct MaskArgs {

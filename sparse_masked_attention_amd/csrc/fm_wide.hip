@@ -1,5 +1,5 @@
-// Wide head dims: bf16 with d = dv = 512, fp32 with d = dv = 256 and with
-// (d, dv) = (192, 128); and the backward at bf16 d = dv = 256.
+// Wide head dims: bf16 with d = dv = 512 and 256, fp32 with d = dv = 256 and
+// with (d, dv) = (192, 128).
 //
 // The pages list large head dims among the method's features (FlashMask
 // README, "News" and "Key Features"); the computation is the same as at
@@ -256,12 +256,16 @@ __device__ inline __amdgpu_buffer_rsrc_t vec_rsrc(const V* base, long long off, 
 }
 
 // ---------------------------------------------------------------- forward
-// Workgroup: 64 query rows (16 per wave) and every output column. Per visible
-// 32-key tile (K, V and the keys' bounds in LDS): S^T = K Q^T (Q in
-// registers), the tile's mask, online softmax, O^T += V^T P^T.
+// Workgroup: 128 query rows (32 per wave, as two 16-row blocks) and every
+// output column. Per visible 32-key tile (K, V and the keys' bounds in LDS):
+// S^T = K Q^T (Q in registers), the tile's mask, online softmax,
+// O^T += V^T P^T. Each K and V operand read from LDS feeds one MFMA per row
+// block.
 template <typename T, int D, int DV>
 struct WFwd {
-  static constexpr int BR = 64, BC = 32;
+  // 16-row blocks per wave: two where Q and O of 32 rows fit the registers
+  static constexpr int RB = (int)sizeof(T) * D <= 512 || sizeof(T) == 4 ? 2 : 1;
+  static constexpr int WR = 16 * RB, BR = 4 * WR, BC = 32;
   static constexpr int RSK = D * (int)sizeof(T) + 16;    // LDS row strides (bytes): K is read by rows,
   static constexpr int RSV = DV * (int)sizeof(T) + 32;   // V by transposed 4-row blocks
   static constexpr int CPK = D * (int)sizeof(T) / 16, CPV = DV * (int)sizeof(T) / 16;
@@ -291,10 +295,11 @@ __device__ inline void mask_rows(f32x4 (&s)[2], const FM_LDS int* vl, int kbase,
   }
 }
 
-// Classes of 32-key tile t for a query-major workgroup (rows [r0, r1), waves
-// of 16 rows from r0) from its 64-key table entry; the tile counters take
-// the entry's own class once (even t), at the reported 64 x 64 tile shape.
-__device__ inline int qmajor_class(const int32_t* table, const WideParams& p, int r0, int r1, int t,
+// Classes of 32-key tile t for a query-major workgroup (rows [r0, r1), four
+// waves of wr rows from r0) from its 64-key table entry; the tile counters
+// take the entry's own class once (even t), at the 64-key width of the
+// reported tile shape.
+__device__ inline int qmajor_class(const int32_t* table, const WideParams& p, int r0, int r1, int wr, int t,
                                    unsigned& bits, unsigned (&cnt)[3]) {
   const BlockBounds bb = load_bounds(table + (long long)(t >> 1) * 8);
   const bool causal = p.causal != 0;
@@ -310,10 +315,10 @@ __device__ inline int qmajor_class(const int32_t* table, const WideParams& p, in
   const bool ragged = c1 - c0 < 32;
 #pragma unroll
   for (int ww = 0; ww < 4; ++ww) {
-    const int a0 = r0 + 16 * ww;
+    const int a0 = r0 + wr * ww;
     int cl = 0;
     if (a0 < p.Nq) {
-      cl = tile_class(bb, a0, min(p.Nq, a0 + 16), c0, c1, causal);
+      cl = tile_class(bb, a0, min(p.Nq, a0 + wr), c0, c1, causal);
       if (ragged && cl == 2) cl = 1;
     }
     bits |= (unsigned)cl << (2 * ww);
@@ -335,7 +340,7 @@ template <typename T, int D, int DV>
 __global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_fwd_kernel(WideParams p) {
   using X = W16<T>;
   using C = WFwd<T, D, DV>;
-  constexpr int KC = X::KC, PF = 6;
+  constexpr int KC = X::KC, PF = wide_occupancy<T, D, DV>() > 1 ? 3 : 6, RB = C::RB;
   __shared__ __attribute__((aligned(16))) char stage0[C::STAGE];
   __shared__ __attribute__((aligned(16))) char stage1[C::STAGE];
   __shared__ int list_[C::LIST];
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_fwd_ke
   const int Nq = p.Nq, Nk = p.Nk;
   const long long qslice = (long long)bh * Nq, kslice = (long long)bh * Nk;
   const int r0 = qb * C::BR, r1 = min(Nq, r0 + C::BR);
-  const int i = r0 + 16 * w + n16;   // this lane's row
+  const int i0 = r0 + C::WR * w + n16;   // this lane's row in row block 0 (block rb: i0 + 16 rb)
   if (tid < 3) wcount_[tid] = 0;
   const __amdgpu_buffer_rsrc_t rk =
       make_rsrc(uniform_ptr(reinterpret_cast<const T*>(p.k) + kslice * D), (uint32_t)Nk * (uint32_t)(C::CPK * 16));
@@ -369,12 +374,17 @@ __global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_fwd_ke
                                              : vec_rsrc(p.ute, vrow, Nk, p.has_ut != 0);
   const int32_t* table = p.table + ((long long)b * p.hm + hmi) * p.nkb64 * 8;
 
-  typename X::op qf[D / KC];
-  load_row_ops<T, D>(qf, reinterpret_cast<const T*>(p.q) + qslice * D, i, Nq, g);
-  f32x4 oacc[DV / 16];
+  typename X::op qf[RB][D / KC];
+  f32x4 oacc[RB][DV / 16];
+  float m_run[RB], l_run[RB];
 #pragma unroll
-  for (int mb = 0; mb < DV / 16; ++mb) oacc[mb] = f32x4{};
-  float m_run = kNegInf, l_run = 0.f;
+  for (int r = 0; r < RB; ++r) {
+    load_row_ops<T, D>(qf[r], reinterpret_cast<const T*>(p.q) + qslice * D, i0 + 16 * r, Nq, g);
+#pragma unroll
+    for (int mb = 0; mb < DV / 16; ++mb) oacc[r][mb] = f32x4{};
+    m_run[r] = kNegInf;
+    l_run[r] = 0.f;
+  }
   unsigned cnt3[3] = {0u, 0u, 0u};
 
   auto issue = [&](unsigned entry, auto stage_c) {
@@ -392,45 +402,63 @@ __global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_fwd_ke
     const FM_LDS char* vst = kst + C::KT;
     const FM_LDS int* vl = (const FM_LDS int*)(kst + C::KT + C::VT);
     const int c0 = (int)(entry & 0xFFFFFFu) * C::BC;
-    // S^T for the tile's two 16-key blocks, the two chains alternating
-    f32x4 s[2] = {f32x4{}, f32x4{}};
+    // S^T for the tile's two 16-key blocks (the two chains alternating),
+    // each K operand for every row block
+    f32x4 s[RB][2];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) s[r][0] = s[r][1] = f32x4{};
     chain<2 * (D / KC), PF>([&](int t) { return row_op<T>(kst, C::RSK, 16 * (t & 1) + n16, t >> 1, g); },
-                            [&](int t, typename X::op a) { s[t & 1] = X::mma(a, qf[t >> 1], s[t & 1]); });
-    if (wc == 1) mask_rows(s, vl, c0, i, p, g);
-    // online softmax, base 2: the offset (and O and the row sum with it)
-    // moves only when some row's maximum outgrew it by more than the slack;
-    // a row with nothing open keeps offset -inf
-    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = max_x4(mx);
-    if (__ballot((mx - m_run) * p.sl2 > 8.0f) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == kNegInf ? 1.f : fast_exp2((m_run - m_new) * p.sl2);
-      l_run *= alpha;
+                            [&](int t, typename X::op a) {
 #pragma unroll
-      for (int mb = 0; mb < DV / 16; ++mb) oacc[mb] *= alpha;
-      m_run = m_new;
-    }
-    const float msl = (m_run == kNegInf ? 0.f : m_run) * p.sl2;
+                              for (int r = 0; r < RB; ++r) s[r][t & 1] = X::mma(a, qf[r][t >> 1], s[r][t & 1]);
+                            });
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int r = 0; r < RB; ++r) {
+      if (wc == 1) mask_rows(s[r], vl, c0, i0 + 16 * r, p, g);
+      // online softmax, base 2: the offset (and O and the row sum with it)
+      // moves only when some row's maximum outgrew it by more than the
+      // slack; a row with nothing open keeps offset -inf
+      float mx = fmaxf(fmaxf(fmaxf(s[r][0][0], s[r][0][1]), fmaxf(s[r][0][2], s[r][0][3])),
+                       fmaxf(fmaxf(s[r][1][0], s[r][1][1]), fmaxf(s[r][1][2], s[r][1][3])));
+      mx = max_x4(mx);
+      if (__ballot((mx - m_run[r]) * p.sl2 > 8.0f) != 0) {
+        const float m_new = fmaxf(m_run[r], mx);
+        const float alpha = m_new == kNegInf ? 1.f : fast_exp2((m_run[r] - m_new) * p.sl2);
+        l_run[r] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float pv = fast_exp2(__builtin_fmaf(s[jb][e], p.sl2, -msl));
-        // bf16: the row sum takes the rounded values the PV product uses
-        if constexpr (!std::is_same<T, float>::value) pv = (float)(bf16)pv;
-        s[jb][e] = pv;
-        l_run += pv;
+        for (int mb = 0; mb < DV / 16; ++mb) oacc[r][mb] *= alpha;
+        m_run[r] = m_new;
       }
-    // O^T += V^T P^T over the tile's 32 keys
+      const float msl = (m_run[r] == kNegInf ? 0.f : m_run[r]) * p.sl2;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pv = fast_exp2(__builtin_fmaf(s[r][jb][e], p.sl2, -msl));
+          // bf16: the row sum takes the rounded values the PV product uses
+          if constexpr (!std::is_same<T, float>::value) pv = (float)(bf16)pv;
+          s[r][jb][e] = pv;
+          l_run[r] += pv;
+        }
+    }
+    // O^T += V^T P^T over the tile's 32 keys, each V operand for every row block
     if constexpr (std::is_same<T, float>::value) {
       constexpr int NB = DV / 16;
       chain<NB * 8, PF>([&](int t) { return col_f32(vst, C::RSV, 16 * (t % NB) + n16, t / NB, g); },
-                        [&](int t, float a) { oacc[t % NB] = X::mma(a, acc_op<T>(s, t / NB), oacc[t % NB]); });
+                        [&](int t, float a) {
+#pragma unroll
+                          for (int r = 0; r < RB; ++r)
+                            oacc[r][t % NB] = X::mma(a, acc_op<T>(s[r], t / NB), oacc[r][t % NB]);
+                        });
     } else {
-      const bf16x8 pop = acc_op<T>(s, 0);
+      bf16x8 pop[RB];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) pop[r] = acc_op<T>(s[r], 0);
       chain<DV / 16, PF>([&](int t) { return col_tr(vst, C::RSV, 16 * t, lane); },
-                         [&](int t, bf16x8 a) { oacc[t] = X::mma(a, pop, oacc[t]); });
+                         [&](int t, bf16x8 a) {
+#pragma unroll
+                           for (int r = 0; r < RB; ++r) oacc[r][t] = X::mma(a, pop[r], oacc[r][t]);
+                         });
     }
   };
 
@@ -438,31 +466,35 @@ __global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_fwd_ke
   int cnt = 0;
   for (int base = 0; base < nkt; base += 256) {
     cnt = scan_chunk(list, (FM_LDS int*)wsum_, cnt, base, nkt,
-                     [&](int t, unsigned& bits) { return qmajor_class(table, p, r0, r1, t, bits, cnt3); });
+                     [&](int t, unsigned& bits) { return qmajor_class(table, p, r0, r1, C::WR, t, bits, cnt3); });
     if (cnt > C::LIST - 256 || base + 256 >= nkt) {
       run_list(list, cnt, issue, compute);
       cnt = 0;
     }
   }
 
-  const float lt = sum_x4(l_run);
-  float inv, row_lse;
-  finish_row(lt, m_run, p.scale, p.sink != nullptr ? p.sink[h] : kNegInf, p.sink != nullptr, inv, row_lse);
-  if (i < Nq) {
-    // lane: row i, columns 16 mb + 4 g + e
-    T* og = reinterpret_cast<T*>(p.o) + (qslice + i) * DV + 4 * g;
 #pragma unroll
-    for (int mb = 0; mb < DV / 16; ++mb) {
-      if constexpr (std::is_same<T, float>::value) {
-        *reinterpret_cast<f32x4*>(og + 16 * mb) = oacc[mb] * inv;
-      } else {
-        bf16x4 v4;
+  for (int r = 0; r < RB; ++r) {
+    const int i = i0 + 16 * r;
+    const float lt = sum_x4(l_run[r]);
+    float inv, row_lse;
+    finish_row(lt, m_run[r], p.scale, p.sink != nullptr ? p.sink[h] : kNegInf, p.sink != nullptr, inv, row_lse);
+    if (i < Nq) {
+      // lane: row i, columns 16 mb + 4 g + e
+      T* og = reinterpret_cast<T*>(p.o) + (qslice + i) * DV + 4 * g;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[mb][e] * inv);
-        *reinterpret_cast<bf16x4*>(og + 16 * mb) = v4;
+      for (int mb = 0; mb < DV / 16; ++mb) {
+        if constexpr (std::is_same<T, float>::value) {
+          *reinterpret_cast<f32x4*>(og + 16 * mb) = oacc[r][mb] * inv;
+        } else {
+          bf16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(oacc[r][mb][e] * inv);
+          *reinterpret_cast<bf16x4*>(og + 16 * mb) = v4;
+        }
       }
+      if (g == 0) p.lse[qslice + i] = row_lse;
     }
-    if (g == 0) p.lse[qslice + i] = row_lse;
   }
   flush_counts(p.counts, wcount_, cnt3);
 }
@@ -591,7 +623,7 @@ __global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_dq_ker
   int cnt = 0;
   for (int base = 0; base < nkt; base += 256) {
     cnt = scan_chunk(list, (FM_LDS int*)wsum_, cnt, base, nkt,
-                     [&](int t, unsigned& bits) { return qmajor_class(table, p, r0, r1, t, bits, cnt3); });
+                     [&](int t, unsigned& bits) { return qmajor_class(table, p, r0, r1, 16, t, bits, cnt3); });
     if (cnt > C::LIST - 256 || base + 256 >= nkt) {
       run_list(list, cnt, issue, compute);
       cnt = 0;
@@ -887,7 +919,7 @@ static WideParams wide_params(const AttnArgs& a) {
 template <typename T, int D, int DV>
 static hipError_t launch_wide_fwd_t(const AttnArgs& a, hipStream_t stream) {
   WideParams p = wide_params(a);
-  p.nqb = (a.Nq + 63) / 64;
+  p.nqb = (a.Nq + WFwd<T, D, DV>::BR - 1) / WFwd<T, D, DV>::BR;
   const long long grid = (long long)a.B * a.H * p.nqb;
   hipLaunchKernelGGL((wide_fwd_kernel<T, D, DV>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -907,9 +939,10 @@ static hipError_t launch_wide_bwd_t(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// the shapes compiled in (kept in step with wide_dims() and wide_bwd_dims())
+// the shapes compiled in (kept in step with wide_dims())
 hipError_t launch_wide_fwd(const AttnArgs& a, hipStream_t stream) {
   if (a.is_bf16 && a.d == 512 && a.dv == 512) return launch_wide_fwd_t<bf16, 512, 512>(a, stream);
+  if (a.is_bf16 && a.d == 256 && a.dv == 256) return launch_wide_fwd_t<bf16, 256, 256>(a, stream);
   if (!a.is_bf16 && a.d == 256 && a.dv == 256) return launch_wide_fwd_t<float, 256, 256>(a, stream);
   if (!a.is_bf16 && a.d == 192 && a.dv == 128) return launch_wide_fwd_t<float, 192, 128>(a, stream);
   return hipErrorInvalidValue;

@@ -63,12 +63,12 @@ def test_table_block_and_tile_shapes(lib):
     # d = 192 exists with dv = 128: bf16 (the narrower kernels) and fp32 (the wide ones)
     assert _binding.tile_shape(False, 192, torch.bfloat16) == (128, 64)
     assert _binding.tile_shape(True, 192, torch.bfloat16) == (32, 128)
-    assert _binding.tile_shape(False, 192, torch.float32) == (64, 64)
+    assert _binding.tile_shape(False, 192, torch.float32) == (128, 64)
     assert _binding.tile_shape(True, 192, torch.float32) == (32, 64)
-    # the wide head dims: 64-row forward blocks, 64-key backward blocks
+    # the wide head dims: 64-key backward blocks (and 64-row forward blocks at bf16 512)
     assert _binding.tile_shape(False, 512, torch.bfloat16) == (64, 64)
     assert _binding.tile_shape(True, 512, torch.bfloat16) == (32, 64)
-    assert _binding.tile_shape(False, 256, torch.float32) == (64, 64)
+    assert _binding.tile_shape(False, 256, torch.float32) == (128, 64)
     assert _binding.tile_shape(True, 256, torch.float32) == (32, 64)
     with pytest.raises(_binding.FlashMaskError):
         _binding.tile_shape(False, 96, torch.bfloat16)
