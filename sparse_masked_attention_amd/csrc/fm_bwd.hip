@@ -1019,7 +1019,7 @@ static hipError_t launch_bwd_main(const AttnArgs& a, hipStream_t stream) {
   p.sl2 = a.scale * kLog2e;
   p.nkb = (a.Nk + kBwdBlockK - 1) / kBwdBlockK;
   p.nkb64 = (a.Nk + kTableBlock - 1) / kTableBlock;
-  if (wide_dims(a.d, a.dv, a.is_bf16)) {
+  if (wide_bwd_dims(a.d, a.dv, a.is_bf16)) {
     // delta and the base-2 LSE, then the wide dQ and dK/dV passes
     p.nqb = (p.Nq + 31) / 32;
     // (the preprocess reads rows of O and dO, dv wide)

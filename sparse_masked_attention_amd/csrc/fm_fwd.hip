@@ -114,11 +114,6 @@ struct QCfg {
 #else
   static constexpr int JBS = (D > 128 || DV > 128 || MODE != kModeFwd) ? 1 : 2;
 #endif
-  // Forward with one wave per SIMD and room for both halves' scores (d = 192,
-  // dv = 128): pipeline the tile's two 32-key halves within the wave. With
-  // two waves per SIMD (d <= 128) the other wave already fills the MFMA pipe
-  // during a softmax, and the pipelined form measured no faster there.
-  static constexpr bool PIPE = MODE == kModeFwd && D > 128 && DV <= 128;
   static constexpr int CHK = D / 8;                       // 16-byte chunks per K row
   static constexpr int CHV = DV / 8;                      // 16-byte chunks per V row
   static constexpr int KT = BC * D * 2;                   // bytes of one K tile
@@ -385,61 +380,6 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
 #pragma unroll
           for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32(tr_read(KW{}, kst, 2 * jb + cc, mb), pf[cc], oacc[mb]);
       }
-    } else if constexpr (C::PIPE) {
-      // Forward, the tile as two 32-key halves in a pipeline: S of half 1 is
-      // formed on the MFMA pipe while the VALU does the softmax of half 0,
-      // and the PV product of half 0 runs while it does half 1. Each half
-      // moves the running offset on its own (exact either way: O and the
-      // row sum always share one offset).
-      f32x16 s2[2];
-      bf16x8 pf2[2][2];
-      auto smma = [&](int jb) {
-        bias(s2[jb], jb);
-        const int row = jb * 32 + l32;
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) s2[jb] = mfma32(row_read(KW{}, kst, row, 2 * c + hh), qf[c], s2[jb]);
-      };
-      auto softmax = [&](int jb) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s2[jb][r]);
-        mx = max_x32(mx);
-        // move the offset (and rescale O and the sum) only when some row's
-        // max outgrew it by more than the slack; a row with nothing open
-        // keeps -inf
-        if (__ballot((mx - m_run) * p.sl2 > kRescaleSlack) != 0) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = m_new == kNegInf ? 1.f : fast_exp2((m_run - m_new) * p.sl2);
-          l_run *= alpha;
-#pragma unroll
-          for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] *= alpha;
-          m_run = m_new;
-        }
-        const float msl = (m_run == kNegInf ? 0.f : m_run) * p.sl2;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          pf2[jb][r / 8][r % 8] = (bf16)fast_exp2(__builtin_fmaf(s2[jb][r], p.sl2, -msl));
-        // row sum of the rounded probabilities (the values the PV MFMA
-        // uses), two per v_dot2_f32_bf16
-        l_run = sum8_bf16(pf2[jb][1], sum8_bf16(pf2[jb][0], l_run));
-      };
-      // O^T += V^T P^T over the half's 32 keys
-      auto pv = [&](int jb) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int mb = 0; mb < DV / 32; ++mb)
-            oacc[mb] = mfma32(tr_read(VW{}, vst, 2 * jb + cc, mb), pf2[jb][cc], oacc[mb]);
-      };
-      smma(0);
-      __builtin_amdgcn_sched_barrier(0);
-      smma(1);
-      softmax(0);
-      __builtin_amdgcn_sched_barrier(0);
-      pv(0);
-      softmax(1);
-      __builtin_amdgcn_sched_barrier(0);
-      pv(1);
     } else {
 #pragma unroll
     for (int hk = 0; hk < C::BC / 32 / JBS; ++hk) {
@@ -919,7 +859,9 @@ template <int MODE>
 static hipError_t dispatch_qmajor(int d, int dv, const FwdParams& p, hipStream_t stream) {
   if (d == 64 && dv == 64) return launch_qmajor<64, 64, MODE>(p, stream);
   if (d == 128 && dv == 128) return launch_qmajor<128, 128, MODE>(p, stream);
-  if (d == 192 && dv == 128) return launch_qmajor<192, 128, MODE>(p, stream);
+  if constexpr (MODE != kModeFwd) {   // (the (192, 128) forward runs the wide-head-dim kernels)
+    if (d == 192 && dv == 128) return launch_qmajor<192, 128, MODE>(p, stream);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -957,7 +899,7 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.sl2 = a.scale * kLog2e;
   p.nkb = (a.Nk + kFwdBlockK - 1) / kFwdBlockK;
-  if (wide_dims(a.d, a.dv, a.is_bf16)) return launch_wide_fwd(a, stream);
+  if (wide_fwd_dims(a.d, a.dv, a.is_bf16)) return launch_wide_fwd(a, stream);
   if (a.is_bf16) {
     return dispatch_qmajor<kModeFwd>(a.d, a.dv, p, stream);
   } else {

@@ -36,11 +36,16 @@ inline bool bf16_dims(int d, int dv) {
 inline bool fp32_dims(int d, int dv) {
   return (d == dv && (d == 64 || d == 128 || d == 256)) || (d == 192 && dv == 128);
 }
-// the shapes served by the wide-head-dim kernels of fm_wide.hip: bf16
-// d = dv = 512 and 256; fp32 d = dv = 256 and (d, dv) = (192, 128)
-inline bool wide_dims(int d, int dv, bool is_bf16) {
+// The shapes served by the wide-head-dim kernels of fm_wide.hip (chosen by
+// measurement against the 32-row kernels): the backward at bf16 d = dv = 512
+// and 256, fp32 d = dv = 256 and (d, dv) = (192, 128); the forward at those
+// and at bf16 (192, 128).
+inline bool wide_bwd_dims(int d, int dv, bool is_bf16) {
   if (is_bf16) return (d == 512 && dv == 512) || (d == 256 && dv == 256);
   return (d == 256 && dv == 256) || (d == 192 && dv == 128);
+}
+inline bool wide_fwd_dims(int d, int dv, bool is_bf16) {
+  return wide_bwd_dims(d, dv, is_bf16) || (is_bf16 && d == 192 && dv == 128);
 }
 
 struct MaskArgs {

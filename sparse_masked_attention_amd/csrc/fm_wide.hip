@@ -1,5 +1,5 @@
 // Wide head dims: bf16 with d = dv = 512 and 256, fp32 with d = dv = 256 and
-// with (d, dv) = (192, 128).
+// with (d, dv) = (192, 128); and the forward at bf16 (d, dv) = (192, 128).
 //
 // The pages list large head dims among the method's features (FlashMask
 // README, "News" and "Key Features"); the computation is the same as at
@@ -948,10 +948,11 @@ static hipError_t launch_wide_bwd_t(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// the shapes compiled in (kept in step with wide_dims())
+// the shapes compiled in (kept in step with wide_fwd_dims() and wide_bwd_dims())
 hipError_t launch_wide_fwd(const AttnArgs& a, hipStream_t stream) {
   if (a.is_bf16 && a.d == 512 && a.dv == 512) return launch_wide_fwd_t<bf16, 512, 512>(a, stream);
   if (a.is_bf16 && a.d == 256 && a.dv == 256) return launch_wide_fwd_t<bf16, 256, 256>(a, stream);
+  if (a.is_bf16 && a.d == 192 && a.dv == 128) return launch_wide_fwd_t<bf16, 192, 128>(a, stream);
   if (!a.is_bf16 && a.d == 256 && a.dv == 256) return launch_wide_fwd_t<float, 256, 256>(a, stream);
   if (!a.is_bf16 && a.d == 192 && a.dv == 128) return launch_wide_fwd_t<float, 192, 128>(a, stream);
   return hipErrorInvalidValue;

@@ -60,7 +60,7 @@ def test_table_block_and_tile_shapes(lib):
     assert _binding.tile_shape(True, 128, torch.bfloat16) == (64, 128)
     assert _binding.tile_shape(True, 256, torch.bfloat16) == (32, 64)   # the wide kernels' backward
     assert _binding.tile_shape(True, 64, torch.float32) == (32, 128)
-    # d = 192 exists with dv = 128: bf16 (the narrower kernels) and fp32 (the wide ones)
+    # d = 192 exists with dv = 128: bf16 (wide forward, 32-row backward) and fp32 (wide both ways)
     assert _binding.tile_shape(False, 192, torch.bfloat16) == (128, 64)
     assert _binding.tile_shape(True, 192, torch.bfloat16) == (32, 128)
     assert _binding.tile_shape(False, 192, torch.float32) == (128, 64)

@@ -1,5 +1,7 @@
 """Parity at the shapes the wide-head-dim kernels serve: bf16 with
-d = dv = 512 and 256, fp32 with d = dv = 256 and with (d, dv) = (192, 128)
+d = dv = 512 and 256, fp32 with d = dv = 256 and with (d, dv) = (192, 128),
+and bf16 (192, 128), whose forward runs there (its backward runs the 32-row
+kernels)
 (the README lists large head dims among FlashMask's features, "News" and
 "Key Features", with Q/K and V head dims apart; the scale stays 1/sqrt(d),
 "Formulation").
@@ -26,7 +28,7 @@ from _lib_fixture import ensure_built
 pytestmark = pytest.mark.gpu
 
 WIDE = [(512, 512, torch.bfloat16), (256, 256, torch.bfloat16), (256, 256, torch.float32),
-        (192, 128, torch.float32)]
+        (192, 128, torch.float32), (192, 128, torch.bfloat16)]
 FAMILIES = ["causal", "document", "share_question", "sliding_window", "block_sparse",
             "prefix_lm_document", "all_open"]
 
