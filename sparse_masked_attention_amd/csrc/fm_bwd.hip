@@ -143,9 +143,9 @@ struct BwdCfg {
 // (8 rows x 4 chunks) of the Q and dO tiles.
 template <int W>
 __device__ inline int swz(int row) {
-  static_assert(W == 64 || W == 128 || W == 192 || W == 256, "row width");
+  static_assert(W == 64 || W == 128 || W == 192, "row width");
   if constexpr (W == 192) return (row >> 1) & 7;   // 24 chunks: stay inside each group of 8
-  else if constexpr (W >= 128) return 4 * (row & 3) + ((row >> 2) & 3);
+  else if constexpr (W == 128) return 4 * (row & 3) + ((row >> 2) & 3);
   else return 4 * (row & 1) + ((row >> 1) & 3);
 }
 

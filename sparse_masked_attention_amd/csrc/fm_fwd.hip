@@ -137,9 +137,9 @@ struct QCfg {
 // reads) both spread over the LDS banks.
 template <int D>
 __device__ inline int fswz(int row) {
-  static_assert(D == 64 || D == 128 || D == 192 || D == 256, "row width");
+  static_assert(D == 64 || D == 128 || D == 192, "row width");
   if constexpr (D == 192) return (row >> 1) & 7;   // 24 chunks: stay inside each group of 8
-  else if constexpr (D >= 128) return 4 * (row & 3) + ((row >> 2) & 3);
+  else if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
   else return 4 * (row & 1) + ((row >> 1) & 3);
 }
 
@@ -414,12 +414,8 @@ __global__ __launch_bounds__(256, (QCfg<D, DV, MODE>::WG_PER_CU)) void qmajor_bf
           __builtin_amdgcn_sched_barrier(0x406);
         }
       };
-      if constexpr (D > 128) {
-        s_chain(std::true_type{});   // one chain above d = 128, where registers are short
-      } else {
-        if (wc == 1) s_chain(std::true_type{});
-        else s_chain(std::false_type{});
-      }
+      if (wc == 1) s_chain(std::true_type{});
+      else s_chain(std::false_type{});
       bf16x8 pf[2 * JBS];
       float mx = max_acc(s);
       mx = max_x32(mx);
