@@ -247,6 +247,47 @@ __device__ inline void run_list(const FM_LDS int* list, int cnt, Issue issue, Co
   }
 }
 
+// The forward's tiles through the same two LDS stages with K (and the keys'
+// bounds) and V waited for apart: tile it's K is needed from the start of
+// its step, its V only after the scores and softmax. Each step passes two
+// barriers: at the first (K of tile it landed everywhere; every wave is done
+// with V of tile it - 1) V of tile it + 1 is issued; at the second (V of
+// tile it landed; every wave is done with K of tile it) K of tile it + 2.
+// Every load then has a step and a half to arrive instead of one. Loads are
+// counted per wave: a K issue is NK instructions, a V issue NV.
+template <int NK, int NV, typename IssueK, typename IssueV, typename Scores, typename Product>
+__device__ inline void run_list_kv(const FM_LDS int* list, int cnt, IssueK issue_k, IssueV issue_v, Scores scores,
+                                   Product product) {
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  auto entry = [&](int it) { return uniform_u32((unsigned)list[it]); };
+  auto step = [&](int it, auto stage_c) {
+    using SN = std::integral_constant<int, 1 - decltype(stage_c)::value>;
+    const unsigned e = entry(it);
+    // K of tile it; V of tile it and K of tile it + 1 may stay in flight
+    if (it + 1 < cnt) wait_vmcnt<NV + NK>();
+    else wait_vmcnt<NV>();
+    lds_barrier();
+    if (it + 1 < cnt) issue_v(entry(it + 1), SN{});
+    scores(e, stage_c);
+    // V of tile it; K of tile it + 1 and V of tile it + 1 may stay in flight
+    if (it + 1 < cnt) wait_vmcnt<NK + NV>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (it + 2 < cnt) issue_k(entry(it + 2), stage_c);
+    product(e, stage_c);
+  };
+  if (cnt > 0) {
+    issue_k(entry(0), S0{});
+    issue_v(entry(0), S0{});
+  }
+  if (cnt > 1) issue_k(entry(1), S1{});
+  for (int it = 0; it < cnt; it += 2) {
+    step(it, S0{});
+    if (it + 1 < cnt) step(it + 1, S1{});
+  }
+}
+
 // Rows [r0, r0 + 32) of a row-major head slice (resource r, CP 16-byte
 // pieces per row) into an LDS tile with row stride rsb bytes: wave w moves
 // rows w, w + 4, ..., one instruction per row. Rows past the slice read 0.
@@ -398,24 +439,31 @@ __global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_fwd_ke
   }
   unsigned cnt3[3] = {0u, 0u, 0u};
 
-  auto issue = [&](unsigned entry, auto stage_c) {
+  // K and the keys' bounds of a tile (8 + 1 load instructions per wave),
+  // and its V (8)
+  auto issue_k = [&](unsigned entry, auto stage_c) {
     FM_LDS char* st = (FM_LDS char*)(decltype(stage_c)::value ? stage1 : stage0);
     const int c0 = (int)(entry & 0xFFFFFFu) * C::BC;
     dma_rows<C::CPK>(rk, st, C::RSK, c0, w, lane);
-    dma_rows<C::CPV>(rv, st + C::KT, C::RSV, c0, w, lane);
     if (lane < 8) load_lds16(rb, st + C::KT + C::VT + w * C::BC * 4, (uint32_t)(c0 + 4 * lane) * 4u);
   };
+  auto issue_v = [&](unsigned entry, auto stage_c) {
+    FM_LDS char* st = (FM_LDS char*)(decltype(stage_c)::value ? stage1 : stage0);
+    const int c0 = (int)(entry & 0xFFFFFFu) * C::BC;
+    dma_rows<C::CPV>(rv, st + C::KT, C::RSV, c0, w, lane);
+  };
 
-  auto compute = [&](unsigned entry, auto stage_c) {
+  // the tile's scores and softmax leave P in s (kept across the second
+  // barrier of the step), then O^T += V^T P^T
+  f32x4 s[RB][2];
+  auto scores = [&](unsigned entry, auto stage_c) {
     const int wc = (int)((entry >> (24 + 2 * w)) & 3u);
     if (wc == 0) return;
     const FM_LDS char* kst = (const FM_LDS char*)(decltype(stage_c)::value ? stage1 : stage0);
-    const FM_LDS char* vst = kst + C::KT;
     const FM_LDS int* vl = (const FM_LDS int*)(kst + C::KT + C::VT);
     const int c0 = (int)(entry & 0xFFFFFFu) * C::BC;
     // S^T for the tile's two 16-key blocks (the two chains alternating),
     // each K operand for every row block
-    f32x4 s[RB][2];
 #pragma unroll
     for (int r = 0; r < RB; ++r) s[r][0] = s[r][1] = f32x4{};
     chain<2 * (D / KC), PF>([&](int t) { return row_op<T>(kst, C::RSK, 16 * (t & 1) + n16, t >> 1, g); },
@@ -452,6 +500,11 @@ __global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_fwd_ke
           l_run[r] += pv;
         }
     }
+  };
+  auto product = [&](unsigned entry, auto stage_c) {
+    const int wc = (int)((entry >> (24 + 2 * w)) & 3u);
+    if (wc == 0) return;
+    const FM_LDS char* vst = (const FM_LDS char*)(decltype(stage_c)::value ? stage1 : stage0) + C::KT;
     // O^T += V^T P^T over the tile's 32 keys, each V operand for every row block
     if constexpr (std::is_same<T, float>::value) {
       constexpr int NB = DV / 16;
@@ -479,7 +532,23 @@ __global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_fwd_ke
     cnt = scan_chunk(list, (FM_LDS int*)wsum_, cnt, base, nkt,
                      [&](int t, unsigned& bits) { return qmajor_class(table, p, r0, r1, C::WR, t, bits, cnt3); });
     if (cnt > C::LIST - 256 || base + 256 >= nkt) {
-      run_list(list, cnt, issue, compute);
+      if constexpr (wide_occupancy<T, D, DV>() == 1) {
+        // one workgroup per CU: nothing else hides a tile's load latency
+        run_list_kv<9, 8>(list, cnt, issue_k, issue_v, scores, product);
+      } else {
+        // two workgroups per CU: the other one's tiles hide it, and a second
+        // barrier per tile measured slower
+        run_list(
+            list, cnt,
+            [&](unsigned e, auto st) {
+              issue_k(e, st);
+              issue_v(e, st);
+            },
+            [&](unsigned e, auto st) {
+              scores(e, st);
+              product(e, st);
+            });
+      }
       cnt = 0;
     }
   }
