@@ -25,9 +25,10 @@
 // forward and dQ pass, key-major dK/dV pass, each tile classified from the
 // key-block table). Tiles of 32 rows move into LDS by LDS DMA (one 16-byte
 // piece per lane, one instruction per tile row), two stages deep: the next
-// visible tile loads while the current one is computed. With rows of at most
-// 512 bytes (bf16 d = 256) two workgroups share a CU; wider rows take a CU
-// each.
+// visible tile loads while the current one is computed (the forward at one
+// workgroup per CU waits for a tile's K and its V apart, so that each load
+// has a tile and a half to arrive). With rows of at most 512 bytes (bf16
+// d = 256, (192, 128)) two workgroups share a CU; wider rows take a CU each.
 #include <type_traits>
 
 #include "fm_device.hpp"
