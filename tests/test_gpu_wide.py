@@ -9,7 +9,8 @@ kernels)
 Forward and backward against the fp64 oracle on every mask family at
 N in {129, 1000}, ragged small N, a sink, Nq != Nk, the tile counters at
 the reported tile shapes, bitwise repeatability, a full-size B=1 H=4
-N=8192 case with whole-head checks on two heads (bf16), and seeded random
+N=8192 case with whole-head checks on two heads (bf16), a causal N=16500
+case whose tile lists take more than one round, and seeded random
 cases (batch, heads, per-head masks, Nq != Nk with arbitrary bounds, causal
 flag, sink). bf16 values follow the replay-aware rule of
 gpu_util.check_bf16; fp32 the fixed 1e-5.
@@ -164,6 +165,36 @@ def test_full_size_bf16_d512(family):
     for x in got:
         assert bool((torch.isfinite(x) | torch.isneginf(x)).all())
     _compare(q, k, v, do, vec, got, torch.bfloat16, heads=[(0, 0), (0, 3)])
+
+
+@pytest.mark.parametrize("d", [512, 256])
+def test_long_sequence_lists_in_rounds_bf16(d):
+    """B=1 H=1 N=16500, causal, bf16 d = dv = 512 (the forward waits for K
+    and V apart) and 256 (one wait per tile): the last query blocks see all
+    516 key tiles of 32 and key block 0 all 516 query tiles, more than one
+    round of the kernels' 512-entry tile lists, so every pass walks its list
+    in rounds. Sampled rows of O and LSE, rows of dQ and keys of dK, dV
+    against the oracle (its sampled backward evaluates every row)."""
+    B, H, N = 1, 1, 16500
+    say(f"wide long list-in-rounds N={N} d={d}")
+    q, k, v, do = _inputs(B, H, N, N, d, d, 8600 + d, True)
+    vec = I.stack_masks([I.causal_only(N)])
+    mv = [oracle.mask_row(x, 0, 0) for x in vec[:4]]
+    got = _run(q, k, v, do, vec, torch.bfloat16)
+    o, lse, dq, dk, dv = (to_np(x)[0, 0] for x in got)
+    for x in (o, dq, dk, dv):
+        assert np.all(np.isfinite(x))
+    rows = [0, 1, 8191, 16383, 16384, 16499]
+    ro, rl = oracle.forward_rows(q[0, 0], k[0, 0], v[0, 0], N, True, *mv, rows=rows)
+    rf, rb = replays(q, k, v, do, vec)
+    check_bf16("O", o[rows], ro, replay=lambda: rf[0]()[0, 0][rows])
+    check_lse(lse[rows], rl, BF16_ATOL)
+    qrows = [0, 16384, 16499]
+    keys = [0, 1, 40, 8000, 16499]
+    rq, rk, rv = oracle.backward_sampled(q[0, 0], k[0, 0], v[0, 0], do[0, 0], True, *mv, rows=qrows, keys=keys)
+    check_bf16("dQ", dq[qrows], rq, replay=lambda: rb[0]()[0, 0][qrows])
+    check_bf16("dK", dk[keys], rk, replay=lambda: rb[1]()[0, 0][keys])
+    check_bf16("dV", dv[keys], rv, replay=lambda: rb[2]()[0, 0][keys])
 
 
 def _draw(seed):
