@@ -291,12 +291,14 @@ __device__ inline void run_list_kv(const FM_LDS int* list, int cnt, IssueK issue
 
 // Rows [r0, r0 + 32) of a row-major head slice (resource r, CP 16-byte
 // pieces per row) into an LDS tile with row stride rsb bytes: wave w moves
-// rows w, w + 4, ..., one instruction per row. Rows past the slice read 0.
+// rows w, w + 4, ..., one instruction per row (kDmaPerWave per wave). Rows
+// past the slice read 0.
+constexpr int kDmaPerWave = 8;
 template <int CP>
 __device__ inline void dma_rows(__amdgpu_buffer_rsrc_t r, FM_LDS char* dst, int rsb, int r0, int w, int lane) {
   static_assert(CP <= 64, "one instruction per row");
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < kDmaPerWave; ++k) {
     const int row = w + 4 * k;
     if (CP == 64 || lane < CP)
       load_lds16(r, dst + row * rsb, (uint32_t)(r0 + row) * (uint32_t)(CP * 16) + 16u * (uint32_t)lane);
@@ -440,8 +442,7 @@ __global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_fwd_ke
   }
   unsigned cnt3[3] = {0u, 0u, 0u};
 
-  // K and the keys' bounds of a tile (8 + 1 load instructions per wave),
-  // and its V (8)
+  // K and the keys' bounds of a tile, and its V
   auto issue_k = [&](unsigned entry, auto stage_c) {
     FM_LDS char* st = (FM_LDS char*)(decltype(stage_c)::value ? stage1 : stage0);
     const int c0 = (int)(entry & 0xFFFFFFu) * C::BC;
@@ -535,7 +536,8 @@ __global__ __launch_bounds__(256, (wide_occupancy<T, D, DV>())) void wide_fwd_ke
     if (cnt > C::LIST - 256 || base + 256 >= nkt) {
       if constexpr (wide_occupancy<T, D, DV>() == 1) {
         // one workgroup per CU: nothing else hides a tile's load latency
-        run_list_kv<9, 8>(list, cnt, issue_k, issue_v, scores, product);
+        // (a K issue also moves the keys' bounds: one instruction more)
+        run_list_kv<kDmaPerWave + 1, kDmaPerWave>(list, cnt, issue_k, issue_v, scores, product);
       } else {
         // two workgroups per CU: the other one's tiles hide it, and a second
         // barrier per tile measured slower
