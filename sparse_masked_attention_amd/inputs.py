@@ -341,6 +341,14 @@ def make_mask(family: str, n: int, rng: np.random.Generator) -> Mask:
         return all_open(n)
     if family == "document3":
         return causal_document(n, doc_lengths_three(n, rng))
+    if family.startswith("equal_document_"):
+        # documents of one length L (the last one shorter when L does not
+        # divide n): every key block then sees the same number of rows, which
+        # separates a kernel's per-block cost from its per-tile cost
+        length = int(family[len("equal_document_"):])
+        if length < 1:
+            raise ValueError(f"document length must be positive: {family!r}")
+        return causal_document(n, [length] * (n // length) + ([n % length] if n % length else []))
     if family == "document":
         if small:
             return causal_document(n, doc_lengths_loguniform(

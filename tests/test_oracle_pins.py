@@ -175,6 +175,23 @@ def test_document_is_blockwise_causal(seed):
         s += L
 
 
+@pytest.mark.parametrize("n,length", [(1000, 128), (8192, 512), (100, 100), (7, 3)])
+def test_equal_document_family(n, length):
+    """The equal-length document family is the causal document mask with
+    lengths [L, L, ..., n mod L]: its dense mask is block-diagonal causal and
+    it opens sum over documents of l(l+1)/2 pairs."""
+    m = I.make_mask(f"equal_document_{length}", n, np.random.default_rng(0))
+    lengths = [length] * (n // length) + ([n % length] if n % length else [])
+    ref = I.causal_document(n, lengths)
+    np.testing.assert_array_equal(m.lts, ref.lts)
+    np.testing.assert_array_equal(m.lte, ref.lte)
+    open_ = ~oracle.dense_mask(n, True, m.lts, m.lte)
+    assert int(open_.sum()) == sum(l * (l + 1) // 2 for l in lengths)
+    doc = np.repeat(np.arange(len(lengths)), lengths)
+    i, j = np.nonzero(open_)
+    assert np.all(doc[i] == doc[j]) and np.all(j <= i)
+
+
 def test_prefix_lm_documents_are_independent():
     rng = np.random.default_rng(7)
     n, d = 90, 8
