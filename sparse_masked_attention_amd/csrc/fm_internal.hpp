@@ -29,7 +29,7 @@ inline int bwd_block_k(int d, int is_bf16) {
   return (is_bf16 ? (d == 512 || d == 256) : (d == 256 || d == 192)) ? 64 : kBwdBlockK;
 }
 
-// Head dims with kernels compiled in: (d, dv) pairs for bf16, d == dv for fp32.
+// Head dims with kernels compiled in, as (d, dv) pairs per dtype.
 inline bool bf16_dims(int d, int dv) {
   return (d == dv && (d == 64 || d == 128 || d == 256 || d == 512)) || (d == 192 && dv == 128);
 }
